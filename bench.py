@@ -1,0 +1,259 @@
+"""Benchmark: mask-aware attention forward + backward on one MI355X.
+
+One step = one pass of the whole path over the workload: flashmask_fwd (block min/max,
+classification, attention forward) then flashmask_bwd (block min/max, classification,
+preprocess, attention backward, dQ conversion); for the context-parallel share the step also
+starts with flashmask_localize.  Inputs are seeded synthetic tensors resident in HBM before the
+timed region.  Throughput counts unmasked score entries only: 4*d FLOPs per entry forward,
+10*d backward.
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "achieved TFLOP/s (unmasked FLOPs) fwd & bwd, % of bf16 MFMA peak, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_c3_hbm_traffic.txt")
+KERNEL_SOURCES = ["attn_bwd.hip", "fm_common.hpp", "launch.hpp"]
+
+
+def unmasked_entries(vectors, nq: int) -> int:
+    """Unmasked (row, key) entries of one head: nq per key minus the union of the key's two
+    closed stretches clipped to [0, nq)."""
+    import numpy as np
+    a1, b1, a2, b2 = (np.clip(np.asarray(v, dtype=np.int64), 0, nq) for v in vectors)
+    l1 = np.maximum(b1 - a1, 0)
+    l2 = np.maximum(b2 - a2, 0)
+    both = (l1 > 0) & (l2 > 0)
+    ov = np.where(both, np.maximum(np.minimum(b1, b2) - np.maximum(a1, a2), 0), 0)
+    return int(nq * len(a1) - (l1 + l2 - ov).sum())
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mask_aware_flashattention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(launch_units: int):
+    """HBM bytes per launch of the backward kernel from the committed counter summary, or None
+    if it is missing or was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except ValueError:
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, vectors, tensors, mask_rows, seconds: float):
+    """The float64 oracle, as it stands, on a bounded sample of the same workload: forward and
+    backward for growing blocks of query rows of head 0 until one run takes >= ``seconds``."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    q = tensors["q"][:, :1]
+    k, v, do = tensors["k"][:, :1], tensors["v"][:, :1], tensors["do"][:, :1]
+    scale = np.float32(w.scale)
+    rows_n = 64
+    rng = np.random.default_rng(0)
+    last = None
+    with threadpool_limits(limits=1):
+        while True:
+            start = int(rng.integers(0, max(1, w.nq - rows_n)))
+            sel = np.arange(start, min(w.nq, start + rows_n))
+            t0 = time.perf_counter()
+            oracle.attention_fwd(q[:, :, sel], k, v, vectors, scale, row_block=16, workers=cores,
+                                 rows=mask_rows[sel])
+            oracle.attention_bwd(q[:, :, sel], k, v, do[:, :, sel], vectors, scale, row_block=16,
+                                 workers=cores, rows=mask_rows[sel])
+            dt = time.perf_counter() - t0
+            M = oracle.dense_mask(*vectors, mask_rows[sel])
+            u = int((~M).sum())
+            last = (dt, u, len(sel))
+            if dt >= seconds or rows_n >= w.nq:
+                break
+            rows_n = min(w.nq, max(rows_n * 2, int(rows_n * seconds / max(dt, 1e-3) * 1.1)))
+    dt, u, nrows = last
+    flops = 14 * w.d * u
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"head 0, {nrows} consecutive query rows of {w.nq}: float64 dense forward + "
+                   f"backward against all {w.nk} keys, {dt:.1f} s; throughput counts the "
+                   f"sample's {u} unmasked entries at 14*d FLOPs each"),
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB "
+                         "(a known-size kernel for scaling HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(no collectives or cross-GPU sharding in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mask_aware_flashattention_amd as fm
+    from mask_aware_flashattention_amd import _lib
+    from workloads import configs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lib = fm.load_library()
+    dev = torch.device("cuda:0")
+    w = configs.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        print("bench workloads are bf16", file=sys.stderr)
+        sys.exit(1)
+
+    gv = configs.global_mask(w)
+    gdev = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in gv]
+    localize_args = None
+    if w.key == "c5":
+        localize_args = (configs.C5_CHUNK_START, configs.C5_CHUNK_LEN, w.params["global_n"])
+        vdev = list(fm.localize(*gdev, *localize_args)[:4])
+        mask_rows = configs.owned_rows(w)
+        vec_cpu_local = [x.cpu().numpy() for x in vdev]
+    else:
+        vdev = gdev
+        mask_rows = np.arange(w.nq)
+        vec_cpu_local = gv
+    U = unmasked_entries(vec_cpu_local, w.nq)
+    flop_f = 4 * w.d * w.B * w.H * U
+    flop_b = 10 * w.d * w.B * w.H * U
+
+    t_cpu = configs.tensors(w)
+    q, k, v, do = (t_cpu[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    shape = _lib.FmShape(w.B, w.H, w.nq, w.nk, w.d, _lib.FM_BF16)
+    ws_f = torch.empty(fm.fwd_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(fm.bwd_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+
+    def step():
+        if localize_args is not None:
+            fm.localize(*gdev, *localize_args)
+        fm.fwd(q, k, v, *vdev, w.scale, out=o, lse=lse, workspace=ws_f)
+        fm.bwd(q, k, v, o, do, lse, *vdev, w.scale, workspace=ws_b, grads=(dq, dk, dv))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-step events: call boundaries (current stream) and the attention kernels alone
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[mk() for _ in range(7)] for _ in range(args.steps)]
+    for row in ev:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        lib.flashmask_set_profile_events(e[3].cuda_event, e[4].cuda_event, e[5].cuda_event,
+                                         e[6].cuda_event)
+        e[0].record()
+        if localize_args is not None:
+            fm.localize(*gdev, *localize_args)
+        fm.fwd(q, k, v, *vdev, w.scale, out=o, lse=lse, workspace=ws_f)
+        e[1].record()
+        fm.bwd(q, k, v, o, do, lse, *vdev, w.scale, workspace=ws_b, grads=(dq, dk, dv))
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lib.flashmask_set_profile_events(None, None, None, None)
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib * (1 << 20)
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    ms = lambda a, b: float(np.mean([r[a].elapsed_time(r[b]) for r in ev]))
+    fwd_call_ms, bwd_call_ms = ms(0, 1), ms(1, 2)
+    fwd_kernel_ms, bwd_kernel_ms = ms(3, 4), ms(5, 6)
+    ms_per_step = wall * 1e3 / args.steps
+    value = (flop_f + flop_b) / (ms_per_step * 1e-3) / 1e12
+
+    traffic = load_traffic(1)
+    bwd_achieved = flop_b / (bwd_kernel_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "nq": w.nq, "nk": w.nk, "d": w.d,
+                   "mask": w.family, "unmasked_per_head": U,
+                   "flop_fwd": flop_f, "flop_bwd": flop_b},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"call_ms": round(fwd_call_ms, 4), "kernel_ms": round(fwd_kernel_ms, 4),
+                "tflops_call": round(flop_f / fwd_call_ms / 1e9, 2),
+                "frac_of_peak_call": round(flop_f / fwd_call_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"call_ms": round(bwd_call_ms, 4), "kernel_ms": round(bwd_kernel_ms, 4),
+                "tflops_call": round(flop_b / bwd_call_ms / 1e9, 2),
+                "frac_of_peak_call": round(flop_b / bwd_call_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"kernel": "attn_bwd_kernel<bf16,128>", "bound": "mfma",
+                     "achieved": round(bwd_achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "roofline_fwd": {"kernel": "attn_fwd_kernel<bf16,128>", "bound": "mfma",
+                         "achieved": round(flop_f / (fwd_kernel_ms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flop_f / (fwd_kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle takes the global vectors with the global row number of every local row
+        out["cpu_baseline"] = cpu_baseline(w, gv, t_cpu, mask_rows, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

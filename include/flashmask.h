@@ -1,0 +1,167 @@
+/*
+ * flashmask.h -- C ABI of the MI355X (gfx950) mask-aware attention library.
+ *
+ * The mask is the column-wise sparse mask of FlashMask: four int32 vectors LTS, LTE, UTS, UTE,
+ * indexed by key column j and holding query-row numbers.  Row i is masked for key j iff
+ * LTS[j] <= i < LTE[j] or UTS[j] <= i < UTE[j] (half-open stretches; a stretch whose start is
+ * not below its end is empty).  Source: "FlashMask-3 sends each GPU its mask without sending
+ * any mask" (learnaivisually.com), four-vector paragraph; "FlashMask-3: Efficient and
+ * Expressive Mask-Aware Distributed Attention", abstract.
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are plain device addresses (hipMalloc'd or torch-allocated memory on the
+ *     current device).  Host pointers are marked "host".
+ *   - Tensors are contiguous, row-major: Q, O, dQ, dO are [B][H][nq][d]; K, V, dK, dV are
+ *     [B][H][nk][d]; LSE is float32 [B][H][nq].  The four vectors are int32[nk], shared by every
+ *     batch and head; any int32 values are accepted.
+ *   - Supported (dtype, d): (FM_BF16, 128) and (FM_FP32, 64).  bf16 tensors are read and written
+ *     as bf16; accumulation is float32.
+ *   - The caller owns every buffer, including the workspace sized by the *_workspace_bytes
+ *     call.  The library allocates no device memory, keeps no state between calls and is
+ *     reentrant; calls that share a workspace must not overlap in time.
+ *   - Outputs are overwritten (never accumulated into).  Inputs are read only.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.  Every call is
+ *     asynchronous on that stream.
+ *   - Errors: every argument check runs on the host before any device work, and a failed check
+ *     returns its code without touching the device.  FM_ERR_HIP reports a failed kernel launch.
+ *     Nothing is printed and nothing aborts.
+ */
+#ifndef FLASHMASK_H
+#define FLASHMASK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FM_OK = 0,
+  FM_ERR_NULL = 1,        /* a required pointer is NULL                                      */
+  FM_ERR_SHAPE = 2,       /* a size is out of range (B, H, nq, nk < 1, or too large)         */
+  FM_ERR_DTYPE = 3,       /* unknown dtype code                                               */
+  FM_ERR_UNSUPPORTED = 4, /* (dtype, d) pair not built                                        */
+  FM_ERR_ALIGN = 5,       /* tensor pointer not 16-byte aligned, or vector not 4-byte aligned */
+  FM_ERR_WORKSPACE = 6,   /* workspace smaller than the *_workspace_bytes value, or NULL      */
+  FM_ERR_CHUNKS = 7,      /* chunk table not sorted / disjoint / non-empty / inside range     */
+  FM_ERR_HIP = 8,         /* a HIP launch failed                                              */
+  FM_ERR_VALUE = 9        /* a scalar argument is invalid (scale not finite and positive)    */
+} fm_status;
+
+typedef enum { FM_BF16 = 0, FM_FP32 = 1 } fm_dtype;
+
+typedef struct {
+  int32_t B, H, nq, nk, d;
+  int32_t dtype; /* fm_dtype */
+} fm_shape;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* flashmask_strerror(int32_t status);
+
+/*
+ * Tile shape used by the attention kernels for (dtype, d): the forward runs BM_fwd query rows
+ * against BN_fwd key columns per tile, the backward BM_bwd x BN_bwd.  These are the tile shapes
+ * at which tiles are classified (see flashmask_classify).  Returns FM_ERR_DTYPE /
+ * FM_ERR_UNSUPPORTED / FM_ERR_NULL, or FM_OK.
+ */
+int32_t flashmask_tile_sizes(int32_t dtype, int32_t d, int32_t* BM_fwd, int32_t* BN_fwd,
+                             int32_t* BM_bwd, int32_t* BN_bwd);
+
+/*
+ * Forward attention.  "FlashMask-3: Efficient and Expressive Mask-Aware Distributed
+ * Attention", abstract (mask-aware kernel); "FlashMask-3 sends each GPU its mask ...",
+ * tile-classification paragraph (fully masked tiles never loaded, the row test only in partly
+ * masked tiles).
+ *
+ * For every batch b, head h and query row i:
+ *   S_ij = scale * Q_i . K_j over unmasked j;  LSE_i = ln sum_j exp(S_ij);
+ *   O_i = sum_j exp(S_ij - LSE_i) V_j.
+ * A row with every key masked gets O_i = 0 and LSE_i = -inf.
+ * scale: finite and > 0 (else FM_ERR_VALUE).
+ * Q [B,H,nq,d], K/V [B,H,nk,d] in `dtype`; O [B,H,nq,d] in `dtype`; LSE float32 [B,H,nq].
+ * ws: device workspace of at least flashmask_fwd_workspace_bytes(shape) bytes (256-byte
+ * aligned), clobbered by the call.
+ */
+size_t flashmask_fwd_workspace_bytes(const fm_shape* shape);
+int32_t flashmask_fwd(const fm_shape* shape, const void* Q, const void* K, const void* V,
+                      const int32_t* LTS, const int32_t* LTE, const int32_t* UTS,
+                      const int32_t* UTE, float scale, void* O, float* LSE, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/*
+ * Backward attention: the exact gradient of L = sum(O * dO) with P recomputed from the saved
+ * LSE.  The pages report forward and backward speed ("FlashMask-3 ..." zicq.com summary,
+ * end-to-end paragraph) without describing the backward; this is the standard recompute form:
+ *   P = exp(S - LSE) (0 where masked), dP = dO V^T, D_i = sum_d dO_id O_id,
+ *   dS = P * (dP - D), dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K.
+ * O and LSE are the forward's outputs.  Rows with LSE = -inf contribute nothing; their dQ is 0.
+ * dQ [B,H,nq,d], dK/dV [B,H,nk,d] in `dtype`, overwritten.  dQ is accumulated in float32 with
+ * atomics inside the call, so its last bits may differ between runs; dK and dV are
+ * deterministic.
+ */
+size_t flashmask_bwd_workspace_bytes(const fm_shape* shape);
+int32_t flashmask_bwd(const fm_shape* shape, const void* Q, const void* K, const void* V,
+                      const void* O, const void* dO, const float* LSE, const int32_t* LTS,
+                      const int32_t* LTE, const int32_t* UTS, const int32_t* UTE, float scale,
+                      void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Rank-local vectors by clip-shift-max.  "FlashMask-3: Efficient and Expressive Mask-Aware
+ * Distributed Attention", abstract (zero-communication mask localisation); "FlashMask-3 sends
+ * each GPU its mask ...", clip-shift-max paragraph (with Theorem 1).
+ *
+ * The rank owns query-row chunks [chunk_start[k], chunk_start[k] + chunk_len[k]) for
+ * k < n_chunks (host arrays; ascending, disjoint, non-empty, inside [0, nq_global];
+ * 1 <= n_chunks <= 64), numbered locally by concatenation.  For every entry x of each global
+ * vector (int32[n], device):
+ *   local(x) = max(0, max_k( min(x, o_k + L_k) - o_k + P_k )),  P_k = L_0 + ... + L_{k-1},
+ * i.e. the number of owned rows below x.  Keys are not renumbered.  Outputs are int32[n]
+ * (device) with values in [0, n_local]; *n_local (host) receives sum_k L_k.  Input and output
+ * vectors may not overlap.
+ */
+int32_t flashmask_localize(const int32_t* LTS_g, const int32_t* LTE_g, const int32_t* UTS_g,
+                           const int32_t* UTE_g, int32_t n, int32_t nq_global,
+                           const int32_t* chunk_start, const int32_t* chunk_len,
+                           int32_t n_chunks, int32_t* LTS_l, int32_t* LTE_l, int32_t* UTS_l,
+                           int32_t* UTE_l, int32_t* n_local, void* stream);
+
+/*
+ * Tile classification and list compaction at an arbitrary tile shape (BM query rows x BN key
+ * columns, both >= 1), the same kernels the attention calls run internally.  "FlashMask-3
+ * sends each GPU its mask ...", tile-classification paragraph.
+ *
+ * With r0 = qb*BM, r1 = min(r0 + BM, nq) and the per-key-block minimum (lo) and maximum (hi) of
+ * each vector over keys [kb*BN, min((kb+1)*BN, nk)):
+ *   full(S,E) = hi(S) <= r0 && lo(E) >= r1;   none(S,E) = hi(E) <= r0 || lo(S) >= r1
+ *   cls = 0 if full(LT) || full(UT);  2 if none(LT) && none(UT);  1 otherwise.
+ * Outputs (device; any may be NULL to skip it):
+ *   cls   uint8 [n_qb][n_kb]
+ *   qcnt  int32 [n_qb],  qlist int32 [n_qb][n_kb]: tiles of class != 0 in ascending kb,
+ *         entry = kb*2 + (cls == 1); entries past qcnt[qb] are unspecified.
+ *   kcnt  int32 [n_kb],  klist int32 [n_kb][n_qb]: the same per key block over qb.
+ * n_qb = ceil(nq/BM), n_kb = ceil(nk/BN); n_qb * n_kb must be below 2^31.
+ * ws: at least flashmask_classify_workspace_bytes(nk, BN) bytes.
+ */
+size_t flashmask_classify_workspace_bytes(int32_t nk, int32_t BN);
+int32_t flashmask_classify(const int32_t* LTS, const int32_t* LTE, const int32_t* UTS,
+                           const int32_t* UTE, int32_t nq, int32_t nk, int32_t BM, int32_t BN,
+                           uint8_t* cls, int32_t* qcnt, int32_t* qlist, int32_t* kcnt,
+                           int32_t* klist, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Diagnostic hook for timing the attention kernels alone (a benchmark aid; not needed to use the
+ * library).  After this call, flashmask_fwd records fwd_begin / fwd_end and flashmask_bwd
+ * records bwd_begin / bwd_end (hipEvent_t passed as void*, created by the caller) on the call's
+ * stream immediately before and after its attention kernel (the backward's main kernel, without
+ * its preprocess and dQ conversion).  NULL disables a pair.  This is the library's only state:
+ * process-wide, not synchronised; set it from the thread that makes the calls.
+ */
+int32_t flashmask_set_profile_events(void* fwd_begin, void* fwd_end, void* bwd_begin,
+                                     void* bwd_end);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHMASK_H */

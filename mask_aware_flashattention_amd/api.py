@@ -1,0 +1,155 @@
+"""Python binding of the C ABI on torch tensors.
+
+PyTorch provides device memory and the current stream; the tensors' pointers go straight to
+``libflashmask.so``.  No computation happens here.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import FmShape, check
+
+_DTYPES = {torch.bfloat16: _lib.FM_BF16, torch.float32: _lib.FM_FP32}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a ROCm/CUDA device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _vectors(lts, lte, uts, ute, nk):
+    for v in (lts, lte, uts, ute):
+        if v.dtype != torch.int32 or v.dim() != 1 or v.numel() != nk:
+            raise ValueError(f"mask vectors must be int32 [{nk}]")
+    _require_cuda(lts, lte, uts, ute)
+
+
+def _shape(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, nq, d] and k, v [B, H, nk, d]")
+    B, H, nq, d = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError("q and k/v disagree on B, H or d")
+    if q.dtype not in _DTYPES:
+        raise ValueError("dtype must be bfloat16 or float32")
+    return FmShape(B, H, nq, k.shape[2], d, _DTYPES[q.dtype])
+
+
+def tile_sizes(dtype=torch.bfloat16, d: int = 128):
+    lib = _lib.load()
+    out = [ctypes.c_int32() for _ in range(4)]
+    check(lib.flashmask_tile_sizes(_DTYPES[dtype], d, *[ctypes.byref(x) for x in out]),
+          "flashmask_tile_sizes")
+    return tuple(x.value for x in out)
+
+
+def fwd_workspace_bytes(shape: FmShape) -> int:
+    return _lib.load().flashmask_fwd_workspace_bytes(ctypes.byref(shape))
+
+
+def bwd_workspace_bytes(shape: FmShape) -> int:
+    return _lib.load().flashmask_bwd_workspace_bytes(ctypes.byref(shape))
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def fwd(q, k, v, lts, lte, uts, ute, scale=None, *, out=None, lse=None, workspace=None):
+    """O, LSE = masked attention forward.  q [B,H,nq,d], k/v [B,H,nk,d] (bf16 d=128 or fp32
+    d=64), mask vectors int32 [nk].  Returns (O like q, LSE float32 [B,H,nq])."""
+    lib = _lib.load()
+    shape = _shape(q, k)
+    _require_cuda(q, k, v)
+    _vectors(lts, lte, uts, ute, shape.nk)
+    if scale is None:
+        scale = 1.0 / math.sqrt(shape.d)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    ws = workspace if workspace is not None else _workspace(fwd_workspace_bytes(shape), q.device)
+    st = lib.flashmask_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lts), _ptr(lte),
+                           _ptr(uts), _ptr(ute), ctypes.c_float(scale), _ptr(o), _ptr(lse_t),
+                           _ptr(ws), ws.numel(), _stream(q.device))
+    check(st, "flashmask_fwd")
+    return o, lse_t
+
+
+def bwd(q, k, v, o, do, lse, lts, lte, uts, ute, scale=None, *, workspace=None, grads=None):
+    """dQ, dK, dV of L = sum(O * dO).  ``o`` and ``lse`` are the forward's outputs."""
+    lib = _lib.load()
+    shape = _shape(q, k)
+    _require_cuda(q, k, v, o, do, lse)
+    _vectors(lts, lte, uts, ute, shape.nk)
+    if scale is None:
+        scale = 1.0 / math.sqrt(shape.d)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = grads
+    ws = workspace if workspace is not None else _workspace(bwd_workspace_bytes(shape), q.device)
+    st = lib.flashmask_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                           _ptr(lse), _ptr(lts), _ptr(lte), _ptr(uts), _ptr(ute),
+                           ctypes.c_float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                           ws.numel(), _stream(q.device))
+    check(st, "flashmask_bwd")
+    return dq, dk, dv
+
+
+def localize(lts, lte, uts, ute, chunk_start, chunk_len, nq_global):
+    """Rank-local vectors by clip-shift-max for the rank owning the given query-row chunks."""
+    lib = _lib.load()
+    n = lts.numel()
+    _vectors(lts, lte, uts, ute, n)
+    starts = (ctypes.c_int32 * len(chunk_start))(*[int(x) for x in chunk_start])
+    lens = (ctypes.c_int32 * len(chunk_len))(*[int(x) for x in chunk_len])
+    if len(chunk_start) != len(chunk_len):
+        raise ValueError("chunk_start and chunk_len differ in length")
+    outs = [torch.empty_like(x) for x in (lts, lte, uts, ute)]
+    n_local = ctypes.c_int32()
+    st = lib.flashmask_localize(_ptr(lts), _ptr(lte), _ptr(uts), _ptr(ute), n, int(nq_global),
+                                starts, lens, len(chunk_start), *[_ptr(x) for x in outs],
+                                ctypes.byref(n_local), _stream(lts.device))
+    check(st, "flashmask_localize")
+    return (*outs, n_local.value)
+
+
+def classify(lts, lte, uts, ute, nq, BM, BN, *, cls=True, qlists=True, klists=True):
+    """Tile classes and compacted lists at tile shape (BM, BN); returns a dict of tensors
+    (cls uint8 [n_qb, n_kb], qcnt, qlist [n_qb, n_kb], kcnt, klist [n_kb, n_qb])."""
+    lib = _lib.load()
+    nk = lts.numel()
+    _vectors(lts, lte, uts, ute, nk)
+    dev = lts.device
+    n_qb, n_kb = -(-nq // BM), -(-nk // BN)
+    out = {}
+    if cls:
+        out["cls"] = torch.empty((n_qb, n_kb), dtype=torch.uint8, device=dev)
+    if qlists:
+        out["qcnt"] = torch.empty(n_qb, dtype=torch.int32, device=dev)
+        out["qlist"] = torch.empty((n_qb, n_kb), dtype=torch.int32, device=dev)
+    if klists:
+        out["kcnt"] = torch.empty(n_kb, dtype=torch.int32, device=dev)
+        out["klist"] = torch.empty((n_kb, n_qb), dtype=torch.int32, device=dev)
+    ws = _workspace(lib.flashmask_classify_workspace_bytes(nk, BN), dev)
+    st = lib.flashmask_classify(_ptr(lts), _ptr(lte), _ptr(uts), _ptr(ute), nq, nk, BM, BN,
+                                _ptr(out.get("cls")), _ptr(out.get("qcnt")),
+                                _ptr(out.get("qlist")), _ptr(out.get("kcnt")),
+                                _ptr(out.get("klist")), _ptr(ws), ws.numel(), _stream(dev))
+    check(st, "flashmask_classify")
+    return out

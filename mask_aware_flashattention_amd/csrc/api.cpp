@@ -1,0 +1,292 @@
+// C ABI of the mask-aware attention library: host-side argument checks (all before any device
+// work), workspace layout, and the launch sequence of each call on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/flashmask.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxListEntries = (int64_t(1) << 31) - 1;
+constexpr int32_t kMaxLen = int32_t(1) << 30;
+
+inline size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Geometry {
+  int64_t n_qb, n_kb;
+};
+
+int32_t check_dtype(int32_t dtype, int32_t d) {
+  if (dtype != FM_BF16 && dtype != FM_FP32) return FM_ERR_DTYPE;
+  if ((dtype == FM_BF16 && d != 128) || (dtype == FM_FP32 && d != 64)) return FM_ERR_UNSUPPORTED;
+  return FM_OK;
+}
+
+// Shape checks shared by forward and backward; fills the tile geometry for (BM, BN).
+int32_t check_shape(const fm_shape* s, int32_t BM, int32_t BN, Geometry* g) {
+  if (!s) return FM_ERR_NULL;
+  const int32_t st = check_dtype(s->dtype, s->d);
+  if (st != FM_OK) return st;
+  if (s->B < 1 || s->H < 1 || s->nq < 1 || s->nk < 1) return FM_ERR_SHAPE;
+  if (s->nq > kMaxLen || s->nk > kMaxLen) return FM_ERR_SHAPE;
+  const int64_t n_qb = ceil_div(s->nq, BM), n_kb = ceil_div(s->nk, BN);
+  if (n_qb * n_kb > kMaxListEntries) return FM_ERR_SHAPE;
+  const int64_t bh = int64_t(s->B) * s->H;
+  if (bh * n_qb > 0x7fffffffLL || bh * n_kb > 0x7fffffffLL) return FM_ERR_SHAPE;
+  if (g) *g = Geometry{n_qb, n_kb};
+  return FM_OK;
+}
+
+int32_t check_vectors(const int32_t* a, const int32_t* b, const int32_t* c, const int32_t* d) {
+  if (!a || !b || !c || !d) return FM_ERR_NULL;
+  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(c, 4) || !aligned(d, 4)) return FM_ERR_ALIGN;
+  return FM_OK;
+}
+
+int32_t check_scale(float scale) {
+  return (std::isfinite(scale) && scale > 0.0f) ? FM_OK : FM_ERR_VALUE;
+}
+
+fm::TileShape tiles(int32_t dtype) { return fm::tile_shape(dtype); }
+
+struct FwdWs {
+  size_t mm, qcnt, qlist, total;
+};
+FwdWs fwd_layout(const Geometry& g) {
+  FwdWs w;
+  w.mm = 0;
+  w.qcnt = w.mm + round_up(sizeof(int32_t) * 8 * g.n_kb);
+  w.qlist = w.qcnt + round_up(sizeof(int32_t) * g.n_qb);
+  w.total = w.qlist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb);
+  return w;
+}
+
+struct BwdWs {
+  size_t mm, kcnt, klist, delta, dq_acc, total;
+};
+BwdWs bwd_layout(const fm_shape* s, const Geometry& g) {
+  BwdWs w;
+  const size_t rows = size_t(s->B) * s->H * s->nq;
+  w.mm = 0;
+  w.kcnt = w.mm + round_up(sizeof(int32_t) * 8 * g.n_kb);
+  w.klist = w.kcnt + round_up(sizeof(int32_t) * g.n_kb);
+  w.delta = w.klist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb);
+  w.dq_acc = w.delta + round_up(sizeof(float) * rows);
+  w.total = w.dq_acc + round_up(sizeof(float) * rows * s->d);
+  return w;
+}
+
+inline int32_t hip_status(hipError_t e) { return e == hipSuccess ? FM_OK : FM_ERR_HIP; }
+
+// Optional timing events (flashmask_set_profile_events); null unless a benchmark sets them.
+hipEvent_t g_fwd_begin = nullptr, g_fwd_end = nullptr, g_bwd_begin = nullptr, g_bwd_end = nullptr;
+
+}  // namespace
+
+extern "C" {
+
+const char* flashmask_strerror(int32_t status) {
+  switch (status) {
+    case FM_OK: return "ok";
+    case FM_ERR_NULL: return "a required pointer is NULL";
+    case FM_ERR_SHAPE: return "a size is out of range";
+    case FM_ERR_DTYPE: return "unknown dtype";
+    case FM_ERR_UNSUPPORTED: return "unsupported (dtype, head dim); built: (bf16, 128), (fp32, 64)";
+    case FM_ERR_ALIGN: return "pointer misaligned (tensors need 16 bytes, vectors 4)";
+    case FM_ERR_WORKSPACE: return "workspace missing or too small";
+    case FM_ERR_CHUNKS: return "chunk table not sorted, disjoint, non-empty and in range (1..64 chunks)";
+    case FM_ERR_HIP: return "HIP launch failed";
+    case FM_ERR_VALUE: return "invalid scalar argument (scale must be finite and > 0)";
+    default: return "unknown status";
+  }
+}
+
+int32_t flashmask_tile_sizes(int32_t dtype, int32_t d, int32_t* BM_fwd, int32_t* BN_fwd,
+                             int32_t* BM_bwd, int32_t* BN_bwd) {
+  const int32_t st = check_dtype(dtype, d);
+  if (st != FM_OK) return st;
+  if (!BM_fwd || !BN_fwd || !BM_bwd || !BN_bwd) return FM_ERR_NULL;
+  const fm::TileShape t = tiles(dtype);
+  *BM_fwd = t.bm_fwd;
+  *BN_fwd = t.bn_fwd;
+  *BM_bwd = t.bm_bwd;
+  *BN_bwd = t.bn_bwd;
+  return FM_OK;
+}
+
+size_t flashmask_fwd_workspace_bytes(const fm_shape* s) {
+  if (!s || check_dtype(s->dtype, s->d) != FM_OK) return 0;
+  const fm::TileShape t = tiles(s->dtype);
+  Geometry g;
+  if (check_shape(s, t.bm_fwd, t.bn_fwd, &g) != FM_OK) return 0;
+  return fwd_layout(g).total;
+}
+
+int32_t flashmask_fwd(const fm_shape* s, const void* Q, const void* K, const void* V,
+                      const int32_t* LTS, const int32_t* LTE, const int32_t* UTS,
+                      const int32_t* UTE, float scale, void* O, float* LSE, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!s) return FM_ERR_NULL;
+  int32_t st = check_dtype(s->dtype, s->d);
+  if (st != FM_OK) return st;
+  const fm::TileShape t = tiles(s->dtype);
+  Geometry g;
+  if ((st = check_shape(s, t.bm_fwd, t.bn_fwd, &g)) != FM_OK) return st;
+  if (!Q || !K || !V || !O || !LSE) return FM_ERR_NULL;
+  if ((st = check_vectors(LTS, LTE, UTS, UTE)) != FM_OK) return st;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
+    return FM_ERR_ALIGN;
+  if ((st = check_scale(scale)) != FM_OK) return st;
+  const FwdWs L = fwd_layout(g);
+  if (!ws || ws_bytes < L.total) return FM_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return FM_ERR_ALIGN;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  int32_t* mm = reinterpret_cast<int32_t*>(base + L.mm);
+  int32_t* qcnt = reinterpret_cast<int32_t*>(base + L.qcnt);
+  int32_t* qlist = reinterpret_cast<int32_t*>(base + L.qlist);
+  const fm::MaskVecs mv{LTS, LTE, UTS, UTE};
+
+  hipError_t e = fm::launch_block_minmax(mv, s->nk, t.bn_fwd, mm, hs);
+  if (e == hipSuccess)
+    e = fm::launch_classify(mm, (int32_t)g.n_kb, s->nq, t.bm_fwd, nullptr, qcnt, qlist, nullptr,
+                            nullptr, hs);
+  if (e == hipSuccess) {
+    fm::FwdArgs a{Q, K, V, mv, O, LSE, qcnt, qlist, (int32_t)g.n_kb, s->B, s->H, s->nq, s->nk,
+                  scale};
+    e = fm::launch_attn_fwd(s->dtype, a, hs, g_fwd_begin, g_fwd_end);
+  }
+  return hip_status(e);
+}
+
+size_t flashmask_bwd_workspace_bytes(const fm_shape* s) {
+  if (!s || check_dtype(s->dtype, s->d) != FM_OK) return 0;
+  const fm::TileShape t = tiles(s->dtype);
+  Geometry g;
+  if (check_shape(s, t.bm_bwd, t.bn_bwd, &g) != FM_OK) return 0;
+  return bwd_layout(s, g).total;
+}
+
+int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const void* V,
+                      const void* O, const void* dO, const float* LSE, const int32_t* LTS,
+                      const int32_t* LTE, const int32_t* UTS, const int32_t* UTE, float scale,
+                      void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
+  if (!s) return FM_ERR_NULL;
+  int32_t st = check_dtype(s->dtype, s->d);
+  if (st != FM_OK) return st;
+  const fm::TileShape t = tiles(s->dtype);
+  Geometry g;
+  if ((st = check_shape(s, t.bm_bwd, t.bn_bwd, &g)) != FM_OK) return st;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FM_ERR_NULL;
+  if ((st = check_vectors(LTS, LTE, UTS, UTE)) != FM_OK) return st;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+      !aligned(dO, 16) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) ||
+      !aligned(LSE, 4))
+    return FM_ERR_ALIGN;
+  if ((st = check_scale(scale)) != FM_OK) return st;
+  const BwdWs L = bwd_layout(s, g);
+  if (!ws || ws_bytes < L.total) return FM_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return FM_ERR_ALIGN;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  int32_t* mm = reinterpret_cast<int32_t*>(base + L.mm);
+  int32_t* kcnt = reinterpret_cast<int32_t*>(base + L.kcnt);
+  int32_t* klist = reinterpret_cast<int32_t*>(base + L.klist);
+  float* delta = reinterpret_cast<float*>(base + L.delta);
+  float* dq_acc = reinterpret_cast<float*>(base + L.dq_acc);
+  const fm::MaskVecs mv{LTS, LTE, UTS, UTE};
+
+  hipError_t e = fm::launch_block_minmax(mv, s->nk, t.bn_bwd, mm, hs);
+  if (e == hipSuccess)
+    e = fm::launch_classify(mm, (int32_t)g.n_kb, s->nq, t.bm_bwd, nullptr, nullptr, nullptr, kcnt,
+                            klist, hs);
+  if (e == hipSuccess) {
+    fm::BwdArgs a{Q,  K,  V,      O,     dO,    LSE,  mv,           dQ,    dK,    dV,
+                  dq_acc, delta, kcnt, klist, (int32_t)g.n_qb, s->B, s->H, s->nq, s->nk, scale};
+    e = fm::launch_attn_bwd(s->dtype, a, hs, g_bwd_begin, g_bwd_end);
+  }
+  return hip_status(e);
+}
+
+int32_t flashmask_localize(const int32_t* LTS_g, const int32_t* LTE_g, const int32_t* UTS_g,
+                           const int32_t* UTE_g, int32_t n, int32_t nq_global,
+                           const int32_t* chunk_start, const int32_t* chunk_len,
+                           int32_t n_chunks, int32_t* LTS_l, int32_t* LTE_l, int32_t* UTS_l,
+                           int32_t* UTE_l, int32_t* n_local, void* stream) {
+  if (!chunk_start || !chunk_len || !n_local) return FM_ERR_NULL;
+  if (n < 0 || nq_global < 0) return FM_ERR_SHAPE;
+  if (n_chunks < 1 || n_chunks > fm::kMaxChunks) return FM_ERR_CHUNKS;
+  fm::ChunkTable table;
+  std::memset(&table, 0, sizeof(table));
+  table.n_chunks = n_chunks;
+  int64_t prefix = 0, prev_end = 0;
+  for (int k = 0; k < n_chunks; ++k) {
+    const int64_t o = chunk_start[k], L = chunk_len[k];
+    if (L < 1 || o < 0 || o + L > nq_global || o < prev_end) return FM_ERR_CHUNKS;
+    table.end[k] = (int32_t)(o + L);
+    table.shift[k] = (int32_t)(prefix - o);
+    prefix += L;
+    prev_end = o + L;
+  }
+  if (n > 0) {
+    int32_t st = check_vectors(LTS_g, LTE_g, UTS_g, UTE_g);
+    if (st != FM_OK) return st;
+    if ((st = check_vectors(LTS_l, LTE_l, UTS_l, UTE_l)) != FM_OK) return st;
+  }
+  *n_local = (int32_t)prefix;
+  if (n == 0) return FM_OK;
+  const fm::MaskVecs in{LTS_g, LTE_g, UTS_g, UTE_g};
+  return hip_status(fm::launch_localize(in, n, table, LTS_l, LTE_l, UTS_l, UTE_l,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t flashmask_classify_workspace_bytes(int32_t nk, int32_t BN) {
+  if (nk < 1 || BN < 1) return 0;
+  return round_up(sizeof(int32_t) * 8 * (size_t)ceil_div(nk, BN));
+}
+
+int32_t flashmask_classify(const int32_t* LTS, const int32_t* LTE, const int32_t* UTS,
+                           const int32_t* UTE, int32_t nq, int32_t nk, int32_t BM, int32_t BN,
+                           uint8_t* cls, int32_t* qcnt, int32_t* qlist, int32_t* kcnt,
+                           int32_t* klist, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st = check_vectors(LTS, LTE, UTS, UTE);
+  if (st != FM_OK) return st;
+  if (nq < 1 || nk < 1 || BM < 1 || BN < 1) return FM_ERR_SHAPE;
+  const int64_t n_qb = ceil_div(nq, BM), n_kb = ceil_div(nk, BN);
+  if (n_qb * n_kb > kMaxListEntries || n_qb > 0x7fffffffLL / 4 || n_kb > 0x7fffffffLL / 4)
+    return FM_ERR_SHAPE;
+  if ((kcnt == nullptr) != (klist == nullptr)) return FM_ERR_NULL;
+  if ((qcnt && !aligned(qcnt, 4)) || (qlist && !aligned(qlist, 4)) || (kcnt && !aligned(kcnt, 4)) ||
+      (klist && !aligned(klist, 4)))
+    return FM_ERR_ALIGN;
+  const size_t need = flashmask_classify_workspace_bytes(nk, BN);
+  if (!ws || ws_bytes < need) return FM_ERR_WORKSPACE;
+  if (!aligned(ws, 4)) return FM_ERR_ALIGN;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* mm = static_cast<int32_t*>(ws);
+  const fm::MaskVecs mv{LTS, LTE, UTS, UTE};
+  hipError_t e = fm::launch_block_minmax(mv, nk, BN, mm, hs);
+  if (e == hipSuccess)
+    e = fm::launch_classify(mm, (int32_t)n_kb, nq, BM, cls, qcnt, qlist, kcnt, klist, hs);
+  return hip_status(e);
+}
+
+int32_t flashmask_set_profile_events(void* fwd_begin, void* fwd_end, void* bwd_begin,
+                                     void* bwd_end) {
+  g_fwd_begin = static_cast<hipEvent_t>(fwd_begin);
+  g_fwd_end = static_cast<hipEvent_t>(fwd_end);
+  g_bwd_begin = static_cast<hipEvent_t>(bwd_begin);
+  g_bwd_end = static_cast<hipEvent_t>(bwd_end);
+  return FM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA wrappers and the
+// element traits that let one attention kernel body serve bf16 (d = 128) and fp32 (d = 64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fm {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element traits.  One MFMA k-step covers KSTEP = 2*KPL elements of the contraction: lanes
+// 0..31 hold KPL consecutive elements and lanes 32..63 the next KPL, for both the A and the B
+// operand (v_mfma_f32_32x32x16_bf16: KPL = 8; v_mfma_f32_32x32x2_f32: KPL = 1).  The 32x32
+// fp32 accumulator holds, in lane l and register r, row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+template <typename T> struct Elem;
+
+template <> struct Elem<bf16> {
+  static constexpr int KPL = 8;
+  typedef bf16x8 frag;  // one lane's share of an operand for one k-step
+  __device__ static inline f32x16 mfma(const frag& a, const frag& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline frag load_frag(const bf16* p) {
+    return *reinterpret_cast<const frag*>(p);
+  }
+  __device__ static inline frag zero_frag() {
+    frag z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+    return z;
+  }
+  __device__ static inline bf16 from_float(float x) { return (bf16)x; }
+};
+
+template <> struct Elem<float> {
+  static constexpr int KPL = 1;
+  typedef float frag;
+  __device__ static inline f32x16 mfma(const frag& a, const frag& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline frag load_frag(const float* p) { return *p; }
+  __device__ static inline frag zero_frag() { return 0.0f; }
+  __device__ static inline float from_float(float x) { return x; }
+};
+
+// Accumulator register r of lane group g (= lane/32) sits at row acc_row(r, g) of the 32x32
+// result tile.
+__device__ __host__ constexpr int acc_row(int r, int g) { return 8 * (r / 4) + 4 * g + (r % 4); }
+
+// Permuted row order used for the operand that becomes the accumulator's row index (keys in the
+// forward S^T, queries in the backward S).  Loading MFMA row acc_row(r, g) from original index
+// perm_index(r, g) makes accumulator register r of group g hold index
+//   (r / KPL) * 2*KPL + g*KPL + r % KPL,
+// so that the KPL registers r = s*KPL .. s*KPL + KPL-1 of group g are exactly the KPL
+// consecutive indices that k-step s of the next product needs in that lane group.  The result
+// (P, or dS) can then be fed to the next MFMA as an operand straight from registers.
+template <int KPL>
+__device__ __host__ constexpr int perm_index(int r, int g) {
+  return (r / KPL) * 2 * KPL + g * KPL + (r % KPL);
+}
+
+// Inverse of the above for a row index m in [0, 32): the original index loaded into MFMA row m.
+template <int KPL>
+__device__ __host__ constexpr int row_source(int m) {
+  // m = 8*(r/4) + 4*g + r%4  ->  r = 4*(m/8) + m%4, g = (m/4)%2
+  return perm_index<KPL>(4 * (m / 8) + (m % 4), (m / 4) % 2);
+}
+
+__device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round float to bf16 (round to nearest even) and pack two into a 32-bit word.
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  bf16 a = (bf16)lo, b = (bf16)hi;
+  uint16_t ua = __builtin_bit_cast(uint16_t, a), ub = __builtin_bit_cast(uint16_t, b);
+  return (uint32_t)ua | ((uint32_t)ub << 16);
+}
+
+// Masked-stretch test: q in [s, s + len) with len = max(e - s, 0) computed in 32-bit unsigned
+// arithmetic.  Exact for every int32 s, e and every q >= 0.
+__device__ inline bool in_stretch(int32_t q, int32_t s, uint32_t len) {
+  return (uint32_t)q - (uint32_t)s < len;
+}
+__host__ __device__ inline uint32_t stretch_len(int32_t s, int32_t e) {
+  return e > s ? (uint32_t)e - (uint32_t)s : 0u;
+}
+
+}  // namespace fm

@@ -1,0 +1,84 @@
+// Internal launch wrappers (host side).  Each returns the hipError_t of its launch(es); the
+// C ABI in api.cpp validates every argument before calling them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fm {
+
+struct MaskVecs {
+  const int32_t* lts;
+  const int32_t* lte;
+  const int32_t* uts;
+  const int32_t* ute;
+};
+
+// Per key block of BN keys: min and max of each vector.  mm is int32[8][n_kb], rows
+// (LTS min, LTS max, LTE min, LTE max, UTS min, UTS max, UTE min, UTE max).
+hipError_t launch_block_minmax(MaskVecs v, int32_t nk, int32_t BN, int32_t* mm,
+                               hipStream_t stream);
+
+// Tile classes and compacted lists from the block min/max (NULL outputs are skipped).
+hipError_t launch_classify(const int32_t* mm, int32_t n_kb, int32_t nq, int32_t BM,
+                           uint8_t* cls, int32_t* qcnt, int32_t* qlist, int32_t* kcnt,
+                           int32_t* klist, hipStream_t stream);
+
+constexpr int kMaxChunks = 64;
+struct ChunkTable {
+  int32_t n_chunks;
+  int32_t end[kMaxChunks];    // o_k + L_k
+  int32_t shift[kMaxChunks];  // P_k - o_k
+};
+
+hipError_t launch_localize(MaskVecs in, int32_t n, const ChunkTable& table, int32_t* lts,
+                           int32_t* lte, int32_t* uts, int32_t* ute, hipStream_t stream);
+
+// Forward attention over precomputed lists.  dtype 0 = bf16 (d 128), 1 = fp32 (d 64).
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  MaskVecs mask;
+  void* o;
+  float* lse;
+  const int32_t* qcnt;
+  const int32_t* qlist;
+  int32_t list_stride;  // n_kb
+  int32_t B, H, nq, nk;
+  float scale;
+};
+// ev_begin / ev_end (may be null) are recorded on the stream around the attention kernel.
+hipError_t launch_attn_fwd(int dtype, const FwdArgs& a, hipStream_t stream, hipEvent_t ev_begin,
+                           hipEvent_t ev_end);
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  MaskVecs mask;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;  // float32 [B,H,nq,d]
+  float* delta;   // float32 [B,H,nq]
+  const int32_t* kcnt;
+  const int32_t* klist;
+  int32_t list_stride;  // n_qb
+  int32_t B, H, nq, nk;
+  float scale;
+};
+hipError_t launch_attn_bwd(int dtype, const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin,
+                           hipEvent_t ev_end);
+
+// Tile shapes of the attention kernels (the shapes tiles are classified at).
+struct TileShape {
+  int32_t bm_fwd, bn_fwd, bm_bwd, bn_bwd;
+};
+TileShape tile_shape(int dtype);
+
+}  // namespace fm

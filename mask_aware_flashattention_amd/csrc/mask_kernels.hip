@@ -1,0 +1,250 @@
+// Integer kernels on the four boundary vectors: per-key-block min/max, tile classification with
+// list compaction, and the clip-shift-max localisation.  All three are O(n) (classification is
+// O(tiles)) scans bound by HBM bandwidth or launch latency; none touches the matrix cores.
+//
+// Sources: "FlashMask-3 sends each GPU its mask without sending any mask" (learnaivisually.com),
+// tile-classification paragraph (min/max along the key axis, three tile classes, a queue of the
+// valid blocks) and clip-shift-max paragraph; "FlashMask-3: Efficient and Expressive Mask-Aware
+// Distributed Attention", abstract (zero-communication localisation).
+#include <limits.h>
+
+#include "fm_common.hpp"
+#include "launch.hpp"
+
+namespace fm {
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+
+__device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }
+
+template <typename F>
+__device__ inline int32_t wave_reduce(int32_t x, F op) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = op(x, __shfl_xor(x, off));
+  return x;
+}
+
+struct MinOp {
+  __device__ int32_t operator()(int32_t a, int32_t b) const { return a < b ? a : b; }
+};
+struct MaxOp {
+  __device__ int32_t operator()(int32_t a, int32_t b) const { return a > b ? a : b; }
+};
+
+// One wave per key block; lanes stride over the block's keys.
+__global__ __launch_bounds__(256) void block_minmax_kernel(MaskVecs v, int32_t nk, int32_t BN,
+                                                           int32_t n_kb, int32_t* __restrict__ mm) {
+  const int kb = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (kb >= n_kb) return;
+  const int lane = lane_id();
+  const int64_t j0 = (int64_t)kb * BN;
+  const int64_t j1 = j0 + BN < nk ? j0 + BN : nk;
+  int32_t lo[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+  int32_t hi[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+  for (int64_t j = j0 + lane; j < j1; j += kWave) {
+    const int32_t x[4] = {v.lts[j], v.lte[j], v.uts[j], v.ute[j]};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      lo[t] = x[t] < lo[t] ? x[t] : lo[t];
+      hi[t] = x[t] > hi[t] ? x[t] : hi[t];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    lo[t] = wave_reduce(lo[t], MinOp());
+    hi[t] = wave_reduce(hi[t], MaxOp());
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      mm[(2 * t) * n_kb + kb] = lo[t];
+      mm[(2 * t + 1) * n_kb + kb] = hi[t];
+    }
+  }
+}
+
+struct BlockBounds {
+  int32_t lts_lo, lts_hi, lte_lo, lte_hi, uts_lo, uts_hi, ute_lo, ute_hi;
+};
+
+__device__ inline BlockBounds load_bounds(const int32_t* __restrict__ mm, int n_kb, int kb) {
+  BlockBounds b;
+  b.lts_lo = mm[0 * n_kb + kb];
+  b.lts_hi = mm[1 * n_kb + kb];
+  b.lte_lo = mm[2 * n_kb + kb];
+  b.lte_hi = mm[3 * n_kb + kb];
+  b.uts_lo = mm[4 * n_kb + kb];
+  b.uts_hi = mm[5 * n_kb + kb];
+  b.ute_lo = mm[6 * n_kb + kb];
+  b.ute_hi = mm[7 * n_kb + kb];
+  return b;
+}
+
+// 0 = fully masked, 1 = partly masked, 2 = unmasked, for query rows [r0, r1).
+__device__ inline int tile_class(const BlockBounds& b, int32_t r0, int32_t r1) {
+  const bool lt_full = b.lts_hi <= r0 && b.lte_lo >= r1;
+  const bool ut_full = b.uts_hi <= r0 && b.ute_lo >= r1;
+  const bool lt_none = b.lte_hi <= r0 || b.lts_lo >= r1;
+  const bool ut_none = b.ute_hi <= r0 || b.uts_lo >= r1;
+  return (lt_full || ut_full) ? 0 : ((lt_none && ut_none) ? 2 : 1);
+}
+
+__device__ inline int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Waves [0, row_waves) each own one query block and scan every key block (forward lists,
+// class matrix); the following waves each own one key block and scan every query block
+// (backward lists).  Compaction is a wave ballot + prefix count, so lists come out ascending.
+__global__ __launch_bounds__(256) void classify_kernel(const int32_t* __restrict__ mm, int32_t n_kb,
+                                                       int32_t nq, int32_t BM, int32_t n_qb,
+                                                       int32_t row_waves, int32_t col_waves,
+                                                       uint8_t* __restrict__ cls,
+                                                       int32_t* __restrict__ qcnt,
+                                                       int32_t* __restrict__ qlist,
+                                                       int32_t* __restrict__ kcnt,
+                                                       int32_t* __restrict__ klist) {
+  const int wid = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  if (wid < row_waves) {
+    const int qb = wid;
+    const int32_t r0 = qb * BM;
+    const int32_t r1 = r0 + BM < nq ? r0 + BM : nq;
+    int32_t cnt = 0;
+    const int64_t row = (int64_t)qb * n_kb;
+    for (int base = 0; base < n_kb; base += kWave) {
+      const int kb = base + lane;
+      int c = 0;
+      if (kb < n_kb) {
+        c = tile_class(load_bounds(mm, n_kb, kb), r0, r1);
+        if (cls) cls[row + kb] = (uint8_t)c;
+      }
+      const bool valid = kb < n_kb && c != 0;
+      const uint64_t ballot = __ballot(valid);
+      if (valid && qlist) qlist[row + cnt + lanes_below(ballot)] = kb * 2 + (c == 1);
+      cnt += __popcll(ballot);
+    }
+    if (lane == 0 && qcnt) qcnt[qb] = cnt;
+  } else if (wid < row_waves + col_waves) {
+    const int kb = wid - row_waves;
+    const BlockBounds b = load_bounds(mm, n_kb, kb);
+    int32_t cnt = 0;
+    const int64_t row = (int64_t)kb * n_qb;
+    for (int base = 0; base < n_qb; base += kWave) {
+      const int qb = base + lane;
+      int c = 0;
+      if (qb < n_qb) {
+        const int32_t r0 = qb * BM;
+        const int32_t r1 = r0 + BM < nq ? r0 + BM : nq;
+        c = tile_class(b, r0, r1);
+      }
+      const bool valid = qb < n_qb && c != 0;
+      const uint64_t ballot = __ballot(valid);
+      if (valid) klist[row + cnt + lanes_below(ballot)] = qb * 2 + (c == 1);
+      cnt += __popcll(ballot);
+    }
+    if (lane == 0) kcnt[kb] = cnt;
+  }
+}
+
+// local(x) = max(0, max_k(min(x, o_k + L_k) + P_k - o_k)).  Negative marks are raised to 0
+// first: that leaves the result unchanged (no owned row lies below 0) and keeps every sum inside
+// int32.
+__device__ inline int32_t clip_shift_max(int32_t x, const ChunkTable& t) {
+  x = x > 0 ? x : 0;
+  int32_t best = 0;
+  for (int k = 0; k < t.n_chunks; ++k) {
+    const int32_t c = (x < t.end[k] ? x : t.end[k]) + t.shift[k];
+    best = c > best ? c : best;
+  }
+  return best;
+}
+
+template <int VEC>
+__global__ __launch_bounds__(256) void localize_kernel(MaskVecs in, int32_t n, ChunkTable table,
+                                                       int32_t* __restrict__ o0,
+                                                       int32_t* __restrict__ o1,
+                                                       int32_t* __restrict__ o2,
+                                                       int32_t* __restrict__ o3) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int32_t* src[4] = {in.lts, in.lte, in.uts, in.ute};
+  int32_t* dst[4] = {o0, o1, o2, o3};
+  if constexpr (VEC == 4) {
+    const int64_t nvec = n / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        int4 x = reinterpret_cast<const int4*>(src[t])[i];
+        x.x = clip_shift_max(x.x, table);
+        x.y = clip_shift_max(x.y, table);
+        x.z = clip_shift_max(x.z, table);
+        x.w = clip_shift_max(x.w, table);
+        reinterpret_cast<int4*>(dst[t])[i] = x;
+      }
+    }
+    // tail (n % 4 elements) handled by the first threads
+    const int64_t i = nvec * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dst[t][i] = clip_shift_max(src[t][i], table);
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dst[t][i] = clip_shift_max(src[t][i], table);
+    }
+  }
+}
+
+inline int grid_for(int64_t work, int threads, int cap) {
+  int64_t g = (work + threads - 1) / threads;
+  if (g < 1) g = 1;
+  return (int)(g < cap ? g : cap);
+}
+
+}  // namespace
+
+hipError_t launch_block_minmax(MaskVecs v, int32_t nk, int32_t BN, int32_t* mm,
+                               hipStream_t stream) {
+  const int32_t n_kb = (nk + BN - 1) / BN;
+  const int grid = (n_kb + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL(block_minmax_kernel, dim3(grid), dim3(256), 0, stream, v, nk, BN, n_kb, mm);
+  return hipGetLastError();
+}
+
+hipError_t launch_classify(const int32_t* mm, int32_t n_kb, int32_t nq, int32_t BM,
+                           uint8_t* cls, int32_t* qcnt, int32_t* qlist, int32_t* kcnt,
+                           int32_t* klist, hipStream_t stream) {
+  const int32_t n_qb = (nq + BM - 1) / BM;
+  const int32_t row_waves = (cls || qcnt || qlist) ? n_qb : 0;
+  const int32_t col_waves = (kcnt && klist) ? n_kb : 0;
+  const int64_t waves = (int64_t)row_waves + col_waves;
+  if (waves == 0) return hipSuccess;
+  const int grid = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
+  hipLaunchKernelGGL(classify_kernel, dim3(grid), dim3(256), 0, stream, mm, n_kb, nq, BM, n_qb,
+                     row_waves, col_waves, cls, qcnt, qlist, kcnt, klist);
+  return hipGetLastError();
+}
+
+hipError_t launch_localize(MaskVecs in, int32_t n, const ChunkTable& table, int32_t* lts,
+                           int32_t* lte, int32_t* uts, int32_t* ute, hipStream_t stream) {
+  const uintptr_t all = (uintptr_t)in.lts | (uintptr_t)in.lte | (uintptr_t)in.uts |
+                        (uintptr_t)in.ute | (uintptr_t)lts | (uintptr_t)lte | (uintptr_t)uts |
+                        (uintptr_t)ute;
+  if ((all & 15) == 0) {
+    const int grid = grid_for((n / 4) > 0 ? n / 4 : 1, 256, 4096);
+    hipLaunchKernelGGL(localize_kernel<4>, dim3(grid), dim3(256), 0, stream, in, n, table, lts,
+                       lte, uts, ute);
+  } else {
+    const int grid = grid_for(n, 256, 4096);
+    hipLaunchKernelGGL(localize_kernel<1>, dim3(grid), dim3(256), 0, stream, in, n, table, lts,
+                       lte, uts, ute);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fm

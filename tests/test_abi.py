@@ -1,0 +1,171 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every function that
+include/flashmask.h declares, and every argument check returns its code before any device work.
+
+Every call below is built to fail a host check, so no kernel is ever launched: pointers are
+fake, never dereferenced values."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mask_aware_flashattention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashmask.h")
+
+FM_OK, FM_ERR_NULL, FM_ERR_SHAPE, FM_ERR_DTYPE, FM_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
+FM_ERR_ALIGN, FM_ERR_WORKSPACE, FM_ERR_CHUNKS, FM_ERR_HIP, FM_ERR_VALUE = 5, 6, 7, 8, 9
+
+P = ctypes.c_void_p(0x100000)       # fake, 256-byte aligned "device" address (never touched)
+P2 = ctypes.c_void_p(0x200000)
+MIS = ctypes.c_void_p(0x100002)     # misaligned for tensors (2 bytes)
+NUL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from mask_aware_flashattention_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flashmask_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_strerror(lib):
+    for s in range(10):
+        assert lib.flashmask_strerror(s)
+    assert b"unknown" in lib.flashmask_strerror(1234)
+
+
+def test_tile_sizes(lib):
+    v = [ctypes.c_int32() for _ in range(4)]
+    refs = [ctypes.byref(x) for x in v]
+    assert lib.flashmask_tile_sizes(0, 128, *refs) == FM_OK
+    assert [x.value for x in v] == [128, 64, 64, 128]
+    assert lib.flashmask_tile_sizes(1, 64, *refs) == FM_OK
+    assert lib.flashmask_tile_sizes(0, 64, *refs) == FM_ERR_UNSUPPORTED
+    assert lib.flashmask_tile_sizes(1, 128, *refs) == FM_ERR_UNSUPPORTED
+    assert lib.flashmask_tile_sizes(7, 128, *refs) == FM_ERR_DTYPE
+    assert lib.flashmask_tile_sizes(0, 128, None, *refs[1:]) == FM_ERR_NULL
+
+
+def shape(B=1, H=2, nq=300, nk=200, d=128, dtype=0):
+    return _lib.FmShape(B, H, nq, nk, d, dtype)
+
+
+def test_workspace_sizes(lib):
+    s = shape()
+    n_qb, n_kb = 3, 4      # forward tiles 128 x 64
+    r = lambda x: -(-x // 256) * 256
+    assert lib.flashmask_fwd_workspace_bytes(ctypes.byref(s)) == r(32 * n_kb) + r(4 * n_qb) + r(4 * n_qb * n_kb)
+    n_qb, n_kb = 5, 2      # backward tiles 64 x 128
+    rows = 1 * 2 * 300
+    want = r(32 * n_kb) + r(4 * n_kb) + r(4 * n_qb * n_kb) + r(4 * rows) + r(4 * rows * 128)
+    assert lib.flashmask_bwd_workspace_bytes(ctypes.byref(s)) == want
+    assert lib.flashmask_fwd_workspace_bytes(ctypes.byref(shape(d=64))) == 0
+    assert lib.flashmask_classify_workspace_bytes(1000, 64) == 512
+    assert lib.flashmask_classify_workspace_bytes(0, 64) == 0
+
+
+def fwd(lib, s, q=P, k=P, v=P, vec=P, o=P2, lse=P2, scale=0.1, ws=P, ws_bytes=0):
+    return lib.flashmask_fwd(ctypes.byref(s) if s is not None else None, q, k, v, vec, vec, vec,
+                             vec, ctypes.c_float(scale), o, lse, ws, ws_bytes, NUL)
+
+
+def test_fwd_checks(lib):
+    s = shape()
+    assert fwd(lib, None) == FM_ERR_NULL
+    assert fwd(lib, shape(dtype=5)) == FM_ERR_DTYPE
+    assert fwd(lib, shape(d=64)) == FM_ERR_UNSUPPORTED
+    assert fwd(lib, shape(dtype=1, d=128)) == FM_ERR_UNSUPPORTED
+    for bad in (dict(B=0), dict(H=0), dict(nq=0), dict(nk=0), dict(nq=-5), dict(nk=(1 << 30) + 1)):
+        assert fwd(lib, shape(**bad)) == FM_ERR_SHAPE, bad
+    assert fwd(lib, s, q=NUL) == FM_ERR_NULL
+    assert fwd(lib, s, vec=NUL) == FM_ERR_NULL
+    assert fwd(lib, s, lse=NUL) == FM_ERR_NULL
+    assert fwd(lib, s, k=MIS) == FM_ERR_ALIGN
+    assert fwd(lib, s, vec=ctypes.c_void_p(0x100001)) == FM_ERR_ALIGN
+    assert fwd(lib, s, scale=0.0) == FM_ERR_VALUE
+    assert fwd(lib, s, scale=-1.0) == FM_ERR_VALUE
+    assert fwd(lib, s, scale=float("nan")) == FM_ERR_VALUE
+    assert fwd(lib, s, scale=float("inf")) == FM_ERR_VALUE
+    need = lib.flashmask_fwd_workspace_bytes(ctypes.byref(s))
+    assert fwd(lib, s, ws_bytes=need - 1) == FM_ERR_WORKSPACE
+    assert fwd(lib, s, ws=NUL, ws_bytes=need) == FM_ERR_WORKSPACE
+
+
+def bwd(lib, s, ptrs=None, scale=0.1, ws=P, ws_bytes=0):
+    p = dict(q=P, k=P, v=P, o=P, do=P, lse=P2, vec=P, dq=P2, dk=P2, dv=P2)
+    p.update(ptrs or {})
+    return lib.flashmask_bwd(ctypes.byref(s), p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"],
+                             p["vec"], p["vec"], p["vec"], p["vec"], ctypes.c_float(scale),
+                             p["dq"], p["dk"], p["dv"], ws, ws_bytes, NUL)
+
+
+def test_bwd_checks(lib):
+    s = shape()
+    for name in ("q", "k", "v", "o", "do", "lse", "vec", "dq", "dk", "dv"):
+        assert bwd(lib, s, {name: NUL}) == FM_ERR_NULL, name
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
+        assert bwd(lib, s, {name: MIS}) == FM_ERR_ALIGN, name
+    assert bwd(lib, shape(nq=0)) == FM_ERR_SHAPE
+    assert bwd(lib, s, scale=0.0) == FM_ERR_VALUE
+    need = lib.flashmask_bwd_workspace_bytes(ctypes.byref(s))
+    assert bwd(lib, s, ws_bytes=need - 1) == FM_ERR_WORKSPACE
+
+
+def localize(lib, starts, lens, n=0, nq_global=100, vec=P, n_local=None):
+    out = n_local if n_local is not None else ctypes.c_int32(-1)
+    a = (ctypes.c_int32 * max(len(starts), 1))(*starts)
+    b = (ctypes.c_int32 * max(len(lens), 1))(*lens)
+    st = lib.flashmask_localize(vec, vec, vec, vec, n, nq_global, a, b, len(starts), P2, P2, P2,
+                                P2, ctypes.byref(out), NUL)
+    return st, out.value
+
+
+def test_localize_chunk_checks(lib):
+    assert localize(lib, [10, 50], [20, 30]) == (FM_OK, 50)       # n = 0: no device work
+    assert localize(lib, [0], [100]) == (FM_OK, 100)
+    assert localize(lib, [50, 10], [5, 5])[0] == FM_ERR_CHUNKS     # unsorted
+    assert localize(lib, [10, 12], [5, 5])[0] == FM_ERR_CHUNKS     # overlapping
+    assert localize(lib, [10], [0])[0] == FM_ERR_CHUNKS            # empty chunk
+    assert localize(lib, [-1], [5])[0] == FM_ERR_CHUNKS            # negative offset
+    assert localize(lib, [98], [5])[0] == FM_ERR_CHUNKS            # past nq_global
+    assert localize(lib, [], [])[0] == FM_ERR_CHUNKS               # no chunk
+    assert localize(lib, list(range(0, 130, 2)), [1] * 65, nq_global=200)[0] == FM_ERR_CHUNKS
+    assert localize(lib, list(range(0, 128, 2)), [1] * 64, nq_global=200) == (FM_OK, 64)
+    assert localize(lib, [0], [5], n=-1)[0] == FM_ERR_SHAPE
+    assert localize(lib, [0], [5], n=10, vec=NUL)[0] == FM_ERR_NULL
+    assert localize(lib, [0], [5], n=10, vec=ctypes.c_void_p(0x100001))[0] == FM_ERR_ALIGN
+    st = lib.flashmask_localize(P, P, P, P, 0, 10, (ctypes.c_int32 * 1)(0), (ctypes.c_int32 * 1)(5),
+                                1, P2, P2, P2, P2, None, NUL)
+    assert st == FM_ERR_NULL
+
+
+def test_classify_checks(lib):
+    def call(vec=P, nq=100, nk=100, BM=16, BN=16, kcnt=P2, klist=P2, ws=P, ws_bytes=0):
+        return lib.flashmask_classify(vec, vec, vec, vec, nq, nk, BM, BN, P2, P2, P2, kcnt, klist,
+                                      ws, ws_bytes, NUL)
+    assert call(vec=NUL) == FM_ERR_NULL
+    assert call(nq=0) == FM_ERR_SHAPE
+    assert call(BN=0) == FM_ERR_SHAPE
+    assert call(BM=-1) == FM_ERR_SHAPE
+    assert call(nq=1 << 30, nk=1 << 30, BM=1, BN=1) == FM_ERR_SHAPE
+    assert call(kcnt=NUL) == FM_ERR_NULL          # kcnt and klist go together
+    assert call(ws_bytes=10) == FM_ERR_WORKSPACE
+    assert call(ws=NUL, ws_bytes=1 << 20) == FM_ERR_WORKSPACE

@@ -1,0 +1,35 @@
+"""Host-side checks of the benchmark: its unmasked-entry count (the FLOP denominator) equals the
+oracle's for every workload, and more than one GPU is refused."""
+
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+from workloads import configs
+
+
+@pytest.mark.parametrize("key", sorted(configs.WORKLOADS))
+def test_unmasked_count_matches_oracle(key):
+    w = configs.WORKLOADS[key]
+    v = configs.global_mask(w)
+    if key == "c5":
+        v = oracle.localize(*v, configs.C5_CHUNK_START, configs.C5_CHUNK_LEN, 131072)[:4]
+    assert bench.unmasked_entries(v, w.nq) == oracle.unmasked_count(*v, w.nq)
+
+
+def test_random_vectors_count():
+    r = np.random.default_rng(5)
+    for _ in range(20):
+        nq, nk = int(r.integers(1, 50)), int(r.integers(1, 50))
+        v = [r.integers(-10, nq + 10, size=nk) for _ in range(4)]
+        assert bench.unmasked_entries(v, nq) == oracle.unmasked_count(*v, nq)
+
+
+def test_more_than_one_gpu_refused():
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
