@@ -96,4 +96,31 @@ __host__ __device__ inline uint32_t stretch_len(int32_t s, int32_t e) {
   return e > s ? (uint32_t)e - (uint32_t)s : 0u;
 }
 
+// ---- raw buffer loads: out-of-range offsets return zeros, so tails need no branches ----------
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+
+// Raw (unstructured) buffer over [base, base + bytes): dword 3 is the gfx9-family value for a
+// plain 32-bit-data raw buffer.
+__device__ inline buf_rsrc make_buf(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ inline uint4 buf_load16(buf_rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ inline uint32_t buf_load4(buf_rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// ---- LDS transpose read (gfx950 ds_read_b64_tr_b16) ------------------------------------------
+// Within each block of 16 lanes, lane i receives element i%4 of the four 16-bit elements that
+// lane 4*j + i/4 addressed, for j = 0..3.  So if lane i addresses X[k0 + i/4][m0 + 4*(i%4)] of a
+// row-major (k-major) matrix X, it receives X[k0 + j][m0 + i], j = 0..3: four consecutive k of
+// column m0 + i, which is the operand layout MFMA wants for a contraction over k.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ inline s16x4 lds_read_tr16(const void* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
+}
+
 }  // namespace fm
