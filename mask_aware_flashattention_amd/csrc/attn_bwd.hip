@@ -7,16 +7,24 @@
 // tile-classification paragraph).
 //
 //   K4 bwd_pre:  D_i = sum_d dO_id O_id, and the float32 dQ accumulator cleared.
-//   K5 bwd_main: one workgroup per key block of BN = 128 keys (4 waves x 32 keys); K and V rows
-//                stay in registers, dK^T and dV^T accumulate in registers; the workgroup walks
-//                the query blocks (BM = 64 rows) of its list.  Per tile:
-//                  S = Q K^T and dP = dO V^T (query rows loaded in a permuted order so the
-//                  accumulators double as operands), P = exp2(S*scale*log2e - LSE*log2e),
-//                  dS = P (dP - D); dV^T += dO^T P; dK^T += Q^T dS; then dS goes through LDS
-//                  (keys contiguous) and dQ += dS K is added to the float32 accumulator with
-//                  atomics.
+//   K5 bwd_main: one workgroup per key block of BN = 128 keys (4 waves x 32 keys).  K and V rows
+//                of the wave's keys stay in registers (B operands of S = Q K^T and dP = dO V^T),
+//                dK^T and dV^T accumulate in registers, and so does the slice of K each wave
+//                needs for its share of dQ.  The workgroup walks the query blocks (BM = 64
+//                rows) of its list.  Per tile:
+//                  S, dP on 32x32 MFMAs with the query rows loaded in a permuted order so the
+//                  accumulators double as operands; P = exp2(S*scale*log2e - LSE*log2e) (0 in
+//                  masked entries); dS = P (dP - D); dV^T += dO^T P and dK^T += Q^T dS with the
+//                  transposed operands read from the row-major Q / dO tiles by the gfx950 LDS
+//                  transpose read; dS goes to LDS key-major (16-byte stores) and the next
+//                  iteration reads it back transposed for dQ += dS K, added to the float32
+//                  accumulator with atomics.
+//                Q / dO tiles are double-buffered and the dQ product of tile i runs after the
+//                barrier of tile i+1, so each tile costs one workgroup barrier.
 //   K6 dq_convert: dQ = scale * accumulator, rounded to the output dtype.
 #include <math.h>
+
+#include <type_traits>
 
 #include "fm_common.hpp"
 #include "launch.hpp"
@@ -30,21 +38,48 @@ struct BwdTile {
   static constexpr int BN = 128, BM = 64, NT = 256;
   static constexpr int KPL = Elem<T>::KPL, KSTEP = 2 * KPL;
   static constexpr int CH = 16 / (int)sizeof(T);
-  static constexpr int CPR = D / CH;
-  static constexpr int Q_LD = D + CH;    // Q, dO row-major [BM][Q_LD]
-  static constexpr int QT_LD = BM + CH;  // Q^T, dO^T [D][QT_LD]
-  static constexpr int DS_LD = BN + CH;  // dS [BM][DS_LD], keys contiguous
-  static constexpr int KT_LD = BN + CH;  // K^T [D][KT_LD]
+  static constexpr int CPR = D / CH;               // 16-byte chunks per Q / dO / K row
+  static constexpr int ROW_BYTES = D * (int)sizeof(T);
+  static constexpr int DS_ROW_BYTES = BM * (int)sizeof(T);  // dS^T rows: one key, BM queries
   static constexpr int NQB = BM / 32;
   static constexpr int NDB = D / 32;
   static constexpr int QK_STEPS = D / KSTEP;
   static constexpr int PQ_STEPS = BM / KSTEP;  // k-steps over a tile's queries
   static constexpr int DQ_STEPS = BN / KSTEP;  // k-steps over the block's keys
-  static constexpr int NOB = NQB * NDB / 4;    // dQ output blocks per wave
+  static constexpr int NOB = NQB * NDB / 4;    // 32x32 dQ output blocks per wave
+  static constexpr int TILE_BYTES = BM * ROW_BYTES;
+  static constexpr int DS_BYTES = BN * DS_ROW_BYTES;
+  // bf16 keeps the block's K rows resident in LDS for the dQ product; fp32 (whose tiles are
+  // twice as large) keeps each wave's slice in registers instead.
+  static constexpr bool K_IN_LDS = sizeof(T) == 2;
+  static constexpr int K_BYTES = K_IN_LDS ? BN * ROW_BYTES : 0;
   static_assert(CPR == 16, "thread mapping assumes 256-byte rows");
   static_assert(BM == 4 * (NT / CPR), "staging: 4 rows per thread");
-  static_assert(NOB >= 1, "dQ split");
+  static_assert(NOB >= 1 && NQB % NOB == 0 || NOB % NQB == 0, "dQ split");
 };
+
+// XOR swizzles of 16-byte chunks (bf16 only; fp32 tiles are left plain).  For 256-byte rows
+// (Q, dO, K tiles): chunk c of row r sits at c ^ swz_row(r), a bijection on 16 consecutive rows
+// (conflict-free row reads of 16 rows at one chunk) whose bits 2..3 differ across 4 consecutive
+// rows (conflict-free transpose reads: 4 rows x 4 chunks per 32 lanes).  For the 128-byte dS^T
+// rows the same two properties hold with swz_ds over 8 chunks and the 64-bank pairs of rows.
+template <typename T>
+__device__ __host__ constexpr int swz_row(int r) {
+  return sizeof(T) == 2 ? (((r & 3) << 2) | ((r >> 2) & 3)) : 0;
+}
+template <typename T>
+__device__ __host__ constexpr int swz_ds(int k) {
+  return sizeof(T) == 2 ? ((((k >> 1) & 1) << 2) | ((k >> 2) & 3)) : 0;
+}
+
+// Byte offset of element (row, col) in a tile of `row_bytes`-byte rows with swizzle kind SK
+// (0 = swz_row, 1 = swz_ds).
+template <typename T, int SK>
+__device__ inline int tile_off(int row, int col, int row_bytes) {
+  constexpr int CH = 16 / (int)sizeof(T);
+  const int sw = SK == 0 ? swz_row<T>(row) : swz_ds<T>(row);
+  return row * row_bytes + (((col / CH) ^ sw) * 16) + (col % CH) * (int)sizeof(T);
+}
 
 struct MaskRegs {
   int32_t s1;
@@ -59,16 +94,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   using E = Elem<T>;
   using frag = typename E::frag;
   constexpr int KPL = C::KPL, KSTEP = C::KSTEP, CH = C::CH;
+  using SwzRow = std::integral_constant<int, 0>;
+  using SwzDs = std::integral_constant<int, 1>;
 
+  // LDS: two (Q, dO) tile buffers, two dS^T buffers, the block's K rows, two (LSE, D) rows.
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* q_lds = reinterpret_cast<T*>(smem);
-  T* do_lds = q_lds + C::BM * C::Q_LD;
-  T* qt_lds = do_lds + C::BM * C::Q_LD;
-  T* dot_lds = qt_lds + D * C::QT_LD;
-  T* ds_lds = dot_lds + D * C::QT_LD;
-  T* kt_lds = ds_lds + C::BM * C::DS_LD;
-  float* lse_lds = reinterpret_cast<float*>(kt_lds + D * C::KT_LD);
-  float* dlt_lds = lse_lds + C::BM;
+  unsigned char* qdo_lds = smem;                                         // [2][Q | dO]
+  unsigned char* ds_lds = smem + 4 * C::TILE_BYTES;                      // [2][BN][BM]
+  unsigned char* k_lds = ds_lds + 2 * C::DS_BYTES;                       // [BN][D]
+  float* rows_lds = reinterpret_cast<float*>(k_lds + C::K_BYTES);       // [2][LSE2 | D]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -86,13 +120,23 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   const float* __restrict__ lse = a.lse + (size_t)bh * a.nq;
   const float* __restrict__ dlt = a.delta + (size_t)bh * a.nq;
   float* __restrict__ dqa = a.dq_acc + (size_t)bh * a.nq * D;
+  const buf_rsrc qbuf = make_buf(Qp, (uint32_t)a.nq * C::ROW_BYTES);
+  const buf_rsrc dobuf = make_buf(dOp, (uint32_t)a.nq * C::ROW_BYTES);
+  const buf_rsrc kbuf = make_buf(Kp, (uint32_t)a.nk * C::ROW_BYTES);
+  const buf_rsrc vbuf = make_buf(Vp, (uint32_t)a.nk * C::ROW_BYTES);
 
   // K and V rows of this lane's key as B operands (k-step s: d = s*KSTEP + g*KPL + 0..KPL).
   frag kf[C::QK_STEPS], vf[C::QK_STEPS];
 #pragma unroll
   for (int s = 0; s < C::QK_STEPS; ++s) {
-    kf[s] = key_ok ? E::load_frag(Kp + (size_t)key * D + s * KSTEP + g * KPL) : E::zero_frag();
-    vf[s] = key_ok ? E::load_frag(Vp + (size_t)key * D + s * KSTEP + g * KPL) : E::zero_frag();
+    const uint32_t off = (uint32_t)key * C::ROW_BYTES + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
+    if constexpr (KPL == 8) {
+      kf[s] = __builtin_bit_cast(frag, buf_load16(kbuf, off, 0));
+      vf[s] = __builtin_bit_cast(frag, buf_load16(vbuf, off, 0));
+    } else {
+      kf[s] = __builtin_bit_cast(frag, buf_load4(kbuf, off, 0));
+      vf[s] = __builtin_bit_cast(frag, buf_load4(vbuf, off, 0));
+    }
   }
   MaskRegs mk;
   if (key_ok) {
@@ -100,33 +144,62 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
     const int32_t uts = a.mask.uts[key], ute = a.mask.ute[key];
     mk = {lts, stretch_len(lts, lte), uts, stretch_len(uts, ute)};
   } else {
-    mk = {INT32_MIN, 0xffffffffu, 0, 0u};
+    mk = {INT32_MIN, 0xffffffffu, 0, 0u};  // past the last key: masked for every row
   }
   const bool ragged_block = (kb == n_kb - 1) && (a.nk % C::BN) != 0;
 
+  // staging map: chunk c of a 256-byte row; rows 4*rq + i
   const int c = tid % C::CPR;
-  const int rq = tid / C::CPR;  // staging: rows 4*rq + i
+  const int rq = tid / C::CPR;
 
-  // K^T of the whole key block into LDS once (operand of dQ += dS K).
-  for (int i = 0; i < C::BN / 16; ++i) {
-    // thread covers key kb*BN + 16*i + rq ... one 16-byte chunk each
-    const int kl = 16 * i + rq;
-    const int kr = kb * C::BN + kl;
-    uint4 x = kr < a.nk ? *reinterpret_cast<const uint4*>(Kp + (size_t)kr * D + c * CH)
-                        : make_uint4(0, 0, 0, 0);
-    const T* xe = reinterpret_cast<const T*>(&x);
+  // transpose-read lane geometry: lane i of 16-lane block b addresses row k0 + 8*(b/2) + i/4,
+  // column m0 + 16*(b%2) + 4*(i%4), and receives rows k0 + 8*(l/32) + 0..3 of column m0 + l%32.
+  const int tb = lane >> 4, ti = lane & 15;
+  const int tr_row = 8 * (tb >> 1) + (ti >> 2);
+  const int tr_col = 16 * (tb & 1) + 4 * (ti & 3);
+
+  // Operand of a contraction over the rows of a row-major tile (k = tile row, m = tile column):
+  // k-step rows k0..k0+KSTEP-1, columns m0..m0+31 -> lane (m = m0 + l%32, g) receives rows
+  // k0 + g*KPL + 0..KPL-1 of its column.
+  auto tr_operand = [&](const unsigned char* tile, int row_bytes, int k0, int m0,
+                        auto swz_kind) -> frag {
+    constexpr int SK = decltype(swz_kind)::value;
+    if constexpr (KPL == 8) {
+      const int r = k0 + tr_row, col = m0 + tr_col;
+      const s16x4 lo = lds_read_tr16(tile + tile_off<T, SK>(r, col, row_bytes));
+      const s16x4 hi = lds_read_tr16(tile + tile_off<T, SK>(r + 4, col, row_bytes));
+      return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return *reinterpret_cast<const T*>(tile + tile_off<T, SK>(k0 + g, m0 + l32, row_bytes));
+    }
+  };
+
+  // The d block this wave produces in dQ.  The block's K rows are the B operand of
+  // dQ += dS K (k = the block's keys, n = d): read by transpose reads from LDS (bf16), or read
+  // once into registers through the first (Q, dO) buffer (fp32).
+  const int wave_db = (w * C::NOB) / C::NQB;
+  unsigned char* kstage = C::K_IN_LDS ? k_lds : qdo_lds;
 #pragma unroll
-    for (int e = 0; e < CH; ++e) kt_lds[(c * CH + e) * C::KT_LD + kl] = xe[e];
+  for (int i = 0; i < C::BN / 16; ++i) {
+    const int row = rq + 16 * i;
+    const uint4 x = buf_load16(kbuf, (uint32_t)(kb * C::BN + row) * C::ROW_BYTES + c * 16, 0);
+    *reinterpret_cast<uint4*>(kstage + tile_off<T, 0>(row, c * CH, C::ROW_BYTES)) = x;
+  }
+  frag kq[C::K_IN_LDS ? 1 : C::DQ_STEPS];
+  if constexpr (!C::K_IN_LDS) {
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < C::DQ_STEPS; ++t)
+      kq[t] = tr_operand(kstage, C::ROW_BYTES, t * KSTEP, 32 * wave_db, SwzRow{});
+    __syncthreads();
   }
 
   f32x16 dv_acc[C::NDB], dk_acc[C::NDB];
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dv_acc[db][r] = 0.0f;
-      dk_acc[db][r] = 0.0f;
-    }
+  for (int db = 0; db < C::NDB; ++db) {
+    dv_acc[db] = f32x16{};
+    dk_acc[db] = f32x16{};
+  }
 
   const int cnt = a.kcnt[kb];
   const int32_t* __restrict__ lst = a.klist + (size_t)kb * a.list_stride;
@@ -135,16 +208,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   uint4 qreg[4], doreg[4];
   float lse_r = INFINITY, dlt_r = 0.0f;
   auto load_tile = [&](int entry) {
-    const int qb = entry >> 1;
+    const uint32_t tile_base = (uint32_t)(entry >> 1) * C::BM * C::ROW_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = qb * C::BM + 4 * rq + i;
-      const bool ok = r < a.nq;
-      qreg[i] = ok ? *reinterpret_cast<const uint4*>(Qp + (size_t)r * D + c * CH) : make_uint4(0, 0, 0, 0);
-      doreg[i] = ok ? *reinterpret_cast<const uint4*>(dOp + (size_t)r * D + c * CH) : make_uint4(0, 0, 0, 0);
+      const uint32_t off = (uint32_t)(4 * rq + i) * C::ROW_BYTES + c * 16;
+      qreg[i] = buf_load16(qbuf, off, tile_base);
+      doreg[i] = buf_load16(dobuf, off, tile_base);
     }
     if (tid < C::BM) {
-      const int r = qb * C::BM + tid;
+      const int r = (entry >> 1) * C::BM + tid;
       if (r < a.nq) {
         const float x = lse[r];
         // a fully masked row (LSE = -inf) must give P = 0: exp2(s - inf) = 0
@@ -156,75 +228,81 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
       }
     }
   };
+  auto store_tile = [&](int buf) {
+    unsigned char* qt = qdo_lds + buf * 2 * C::TILE_BYTES;
+    unsigned char* dt = qt + C::TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int off = tile_off<T, 0>(4 * rq + i, c * CH, C::ROW_BYTES);
+      *reinterpret_cast<uint4*>(qt + off) = qreg[i];
+      *reinterpret_cast<uint4*>(dt + off) = doreg[i];
+    }
+    if (tid < C::BM) {
+      rows_lds[buf * 2 * C::BM + tid] = lse_r;
+      rows_lds[buf * 2 * C::BM + C::BM + tid] = dlt_r;
+    }
+  };
 
-  auto store_rows = [&](T* rm, T* tr, const uint4* regs) {
+  // dQ[q][d] += sum_keys dS[q][key] K[key][d] for the tile held in dS^T buffer `buf`; wave w
+  // owns d columns [32*wave_db, +32) and NOB query row blocks of them.
+  auto dq_product = [&](int buf, int qb) {
+    const unsigned char* dst = ds_lds + buf * C::DS_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(&rm[(4 * rq + i) * C::Q_LD + c * CH]) = regs[i];
-    if constexpr (sizeof(T) == 2) {
-      const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&regs[0]);
-      const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&regs[1]);
-      const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&regs[2]);
-      const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&regs[3]);
+    for (int ob = 0; ob < C::NOB; ++ob) {
+      const int qr = (w * C::NOB + ob) % C::NQB;
+      f32x16 acc = {};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1;
-        uint2 out;
-        if ((e & 1) == 0) {
-          out.x = (v0[wd] & 0xffffu) | (v1[wd] << 16);
-          out.y = (v2[wd] & 0xffffu) | (v3[wd] << 16);
-        } else {
-          out.x = (v0[wd] >> 16) | (v1[wd] & 0xffff0000u);
-          out.y = (v2[wd] >> 16) | (v3[wd] & 0xffff0000u);
-        }
-        *reinterpret_cast<uint2*>(&tr[(8 * c + e) * C::QT_LD + 4 * rq]) = out;
+      for (int t = 0; t < C::DQ_STEPS; ++t) {
+        frag kb_op;
+        if constexpr (C::K_IN_LDS)
+          kb_op = tr_operand(k_lds, C::ROW_BYTES, t * KSTEP, 32 * wave_db, SwzRow{});
+        else
+          kb_op = kq[t];
+        acc = E::mfma(tr_operand(dst, C::DS_ROW_BYTES, t * KSTEP, 32 * qr, SwzDs{}), kb_op, acc);
       }
-    } else {
+      // acc register r: query qr*32 + acc_row(r, g), d = 32*wave_db + l32
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint4 out;
-        out.x = reinterpret_cast<const uint32_t*>(&regs[0])[e];
-        out.y = reinterpret_cast<const uint32_t*>(&regs[1])[e];
-        out.z = reinterpret_cast<const uint32_t*>(&regs[2])[e];
-        out.w = reinterpret_cast<const uint32_t*>(&regs[3])[e];
-        *reinterpret_cast<uint4*>(&tr[(4 * c + e) * C::QT_LD + 4 * rq]) = out;
+      for (int r = 0; r < 16; ++r) {
+        const int q = qb * C::BM + qr * 32 + acc_row(r, g);
+        if (q < a.nq) unsafeAtomicAdd(&dqa[(size_t)q * D + wave_db * 32 + l32], acc[r]);
       }
     }
   };
 
-  if (cnt > 0) load_tile(lst[0]);
+  if (cnt > 0) {
+    load_tile(lst[0]);
+    store_tile(0);
+  }
 
   for (int it = 0; it < cnt; ++it) {
     const int entry = lst[it];
     const int qb = entry >> 1;
+    const int buf = it & 1;
     const bool test = (entry & 1) || ragged_block;
-    __syncthreads();  // previous tile fully consumed (including dS and the dQ product)
-    store_rows(q_lds, qt_lds, qreg);
-    store_rows(do_lds, dot_lds, doreg);
-    if (tid < C::BM) {
-      lse_lds[tid] = lse_r;
-      dlt_lds[tid] = dlt_r;
-    }
-    __syncthreads();
+    __syncthreads();  // tile `it` staged in `buf`; dS^T of tile it-1 complete in buf ^ 1
     if (it + 1 < cnt) load_tile(lst[it + 1]);
+    if (it > 0) dq_product(buf ^ 1, lst[it - 1] >> 1);
+
+    const unsigned char* qt = qdo_lds + buf * 2 * C::TILE_BYTES;
+    const unsigned char* dt = qt + C::TILE_BYTES;
+    const float* lse_t = rows_lds + buf * 2 * C::BM;
+    const float* dlt_t = lse_t + C::BM;
 
     // S = Q K^T and dP = dO V^T.  Register r of group g in query row block qr is tile query
     // qr*32 + perm_index(r, g); the column is this lane's key.
     f32x16 sacc[C::NQB], pacc[C::NQB];
 #pragma unroll
     for (int qr = 0; qr < C::NQB; ++qr) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sacc[qr][r] = 0.0f;
-        pacc[qr][r] = 0.0f;
-      }
       const int row = qr * 32 + row_source<KPL>(l32);
-      const T* qp = &q_lds[row * C::Q_LD + g * KPL];
-      const T* dp = &do_lds[row * C::Q_LD + g * KPL];
+      sacc[qr] = f32x16{};
+      pacc[qr] = f32x16{};
 #pragma unroll
       for (int s = 0; s < C::QK_STEPS; ++s) {
-        sacc[qr] = E::mfma(E::load_frag(qp + s * KSTEP), kf[s], sacc[qr]);
-        pacc[qr] = E::mfma(E::load_frag(dp + s * KSTEP), vf[s], pacc[qr]);
+        const int off = tile_off<T, 0>(row, s * KSTEP + g * KPL, C::ROW_BYTES);
+        const frag qa = *reinterpret_cast<const frag*>(qt + off);
+        const frag da = *reinterpret_cast<const frag*>(dt + off);
+        sacc[qr] = E::mfma(qa, kf[s], sacc[qr]);
+        pacc[qr] = E::mfma(da, vf[s], pacc[qr]);
       }
     }
 
@@ -234,68 +312,58 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ql = qr * 32 + perm_index<KPL>(r, g);
-        float p = fast_exp2(fmaf(sacc[qr][r], cexp, -lse_lds[ql]));
+        float p = fast_exp2(fmaf(sacc[qr][r], cexp, -lse_t[ql]));
         if (test) {
           const int32_t q = qb * C::BM + ql;
-          if (in_stretch(q, mk.s1, mk.len1) || in_stretch(q, mk.s2, mk.len2)) p = 0.0f;
+          p = (in_stretch(q, mk.s1, mk.len1) || in_stretch(q, mk.s2, mk.len2)) ? 0.0f : p;
         }
         sacc[qr][r] = p;
-        pacc[qr][r] = p * (pacc[qr][r] - dlt_lds[ql]);
+        pacc[qr][r] = p * (pacc[qr][r] - dlt_t[ql]);
       }
 
-    // dV^T += dO^T P and dK^T += Q^T dS.  k-step t covers tile queries t*KSTEP + g*KPL + e,
+    // Operand fragments of P and dS: k-step t covers tile queries t*KSTEP + g*KPL + e,
     // registers (t*KPL)%16 + e of query row block (t*KPL)/16.
+    frag pf[C::PQ_STEPS], sf[C::PQ_STEPS];
 #pragma unroll
     for (int t = 0; t < C::PQ_STEPS; ++t) {
-      frag pf, sf;
       if constexpr (KPL == 1) {
-        pf = sacc[t / 16][t % 16];
-        sf = pacc[t / 16][t % 16];
+        pf[t] = sacc[t / 16][t % 16];
+        sf[t] = pacc[t / 16][t % 16];
       } else {
 #pragma unroll
         for (int e = 0; e < KPL; ++e) {
-          pf[e] = E::from_float(sacc[(t * KPL) / 16][(t * KPL) % 16 + e]);
-          sf[e] = E::from_float(pacc[(t * KPL) / 16][(t * KPL) % 16 + e]);
+          pf[t][e] = E::from_float(sacc[(t * KPL) / 16][(t * KPL) % 16 + e]);
+          sf[t][e] = E::from_float(pacc[(t * KPL) / 16][(t * KPL) % 16 + e]);
         }
       }
+    }
+
+    // dS^T -> LDS (key-major): this lane's key row, queries t*KSTEP + g*KPL + 0..KPL.
+    {
+      unsigned char* dst = ds_lds + buf * C::DS_BYTES;
+      const int krow = w * 32 + l32;
+#pragma unroll
+      for (int t = 0; t < C::PQ_STEPS; ++t)
+        *reinterpret_cast<frag*>(dst + tile_off<T, 1>(krow, t * KSTEP + g * KPL, C::DS_ROW_BYTES)) = sf[t];
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS: A = rows d of the transposed tiles (contraction over
+    // the tile's queries), read with the transpose read.
+#pragma unroll
+    for (int t = 0; t < C::PQ_STEPS; ++t) {
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
-        const int off = (db * 32 + l32) * C::QT_LD + t * KSTEP + g * KPL;
-        dv_acc[db] = E::mfma(E::load_frag(&dot_lds[off]), pf, dv_acc[db]);
-        dk_acc[db] = E::mfma(E::load_frag(&qt_lds[off]), sf, dk_acc[db]);
+        dv_acc[db] = E::mfma(tr_operand(dt, C::ROW_BYTES, t * KSTEP, 32 * db, SwzRow{}), pf[t], dv_acc[db]);
+        dk_acc[db] = E::mfma(tr_operand(qt, C::ROW_BYTES, t * KSTEP, 32 * db, SwzRow{}), sf[t], dk_acc[db]);
       }
     }
 
-    // dS -> LDS as [query][key] (keys contiguous) for the dQ product.
-#pragma unroll
-    for (int qr = 0; qr < C::NQB; ++qr)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = qr * 32 + perm_index<KPL>(r, g);
-        ds_lds[ql * C::DS_LD + w * 32 + l32] = E::from_float(pacc[qr][r]);
-      }
+    // stage the next tile into the other buffer (last read in the previous iteration)
+    if (it + 1 < cnt) store_tile(buf ^ 1);
+  }
+  if (cnt > 0) {
     __syncthreads();
-
-    // dQ[q][d] += sum_keys dS[q][key] K[key][d]; wave w owns NOB 32x32 output blocks.
-#pragma unroll
-    for (int ob = 0; ob < C::NOB; ++ob) {
-      const int blk = w * C::NOB + ob;
-      const int qr = blk % C::NQB, db = blk / C::NQB;
-      f32x16 acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-      const T* ap = &ds_lds[(qr * 32 + l32) * C::DS_LD + g * KPL];
-      const T* bp = &kt_lds[(db * 32 + l32) * C::KT_LD + g * KPL];
-#pragma unroll
-      for (int t = 0; t < C::DQ_STEPS; ++t)
-        acc = E::mfma(E::load_frag(ap + t * KSTEP), E::load_frag(bp + t * KSTEP), acc);
-      // acc register r: query qr*32 + acc_row(r, g), d = db*32 + l32
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = qb * C::BM + qr * 32 + acc_row(r, g);
-        if (q < a.nq) unsafeAtomicAdd(&dqa[(size_t)q * D + db * 32 + l32], acc[r]);
-      }
-    }
+    dq_product((cnt - 1) & 1, lst[cnt - 1] >> 1);
   }
 
   if (key_ok) {
@@ -375,8 +443,7 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 template <typename T, int D>
 size_t bwd_smem_bytes() {
   using C = BwdTile<T, D>;
-  return sizeof(T) * (2 * C::BM * C::Q_LD + 2 * D * C::QT_LD + C::BM * C::DS_LD + D * C::KT_LD) +
-         sizeof(float) * 2 * C::BM;
+  return 4 * C::TILE_BYTES + 2 * C::DS_BYTES + C::K_BYTES + sizeof(float) * 4 * C::BM;
 }
 
 template <typename T, int D>
