@@ -39,7 +39,7 @@ extern "C" {
 typedef enum {
   FM_OK = 0,
   FM_ERR_NULL = 1,        /* a required pointer is NULL                                      */
-  FM_ERR_SHAPE = 2,       /* a size is out of range (B, H, nq, nk < 1, nq or nk > 2^24, ...) */
+  FM_ERR_SHAPE = 2,       /* a size is out of range (B, H, nq, nk < 1, nq or nk > 2^22, ...) */
   FM_ERR_DTYPE = 3,       /* unknown dtype code                                               */
   FM_ERR_UNSUPPORTED = 4, /* (dtype, d) pair not built                                        */
   FM_ERR_ALIGN = 5,       /* tensor pointer not 16-byte aligned, or vector not 4-byte aligned */

@@ -13,9 +13,9 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxListEntries = (int64_t(1) << 31) - 1;
-// Per (batch, head) a K, V, Q or O slab must stay below 4 GiB (the kernels address it with
-// 32-bit buffer offsets): 2^24 rows of 256 bytes.
-constexpr int32_t kMaxLen = int32_t(1) << 24;
+// Per (batch, head) every slab the kernels address with 32-bit buffer offsets (Q, K, V, O and
+// the float32 dQ accumulator, at most 512 bytes per row) must stay below 4 GiB.
+constexpr int32_t kMaxLen = int32_t(1) << 22;
 
 inline size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

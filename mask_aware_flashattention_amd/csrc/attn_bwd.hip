@@ -120,6 +120,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   const float* __restrict__ lse = a.lse + (size_t)bh * a.nq;
   const float* __restrict__ dlt = a.delta + (size_t)bh * a.nq;
   float* __restrict__ dqa = a.dq_acc + (size_t)bh * a.nq * D;
+  // dQ accumulator rows past nq fall outside this buffer, so their atomics are dropped.
+  const buf_rsrc dqbuf = make_buf(dqa, (uint32_t)a.nq * D * (uint32_t)sizeof(float));
   const buf_rsrc qbuf = make_buf(Qp, (uint32_t)a.nq * C::ROW_BYTES);
   const buf_rsrc dobuf = make_buf(dOp, (uint32_t)a.nq * C::ROW_BYTES);
   const buf_rsrc kbuf = make_buf(Kp, (uint32_t)a.nk * C::ROW_BYTES);
@@ -260,110 +262,112 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
           kb_op = kq[t];
         acc = E::mfma(tr_operand(dst, C::DS_ROW_BYTES, t * KSTEP, 32 * qr, SwzDs{}), kb_op, acc);
       }
-      // acc register r: query qr*32 + acc_row(r, g), d = 32*wave_db + l32
+      // acc register r: query qr*32 + acc_row(r, g) = (qr*32 + 8*(r/4) + r%4) + 4*g,
+      // d = 32*wave_db + l32: the first part is uniform (scalar offset), the rest per lane.
+      const uint32_t lane_off = (uint32_t)((4 * g * D + wave_db * 32 + l32) * sizeof(float));
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int q = qb * C::BM + qr * 32 + acc_row(r, g);
-        if (q < a.nq) unsafeAtomicAdd(&dqa[(size_t)q * D + wave_db * 32 + l32], acc[r]);
+        const uint32_t row = (uint32_t)(qb * C::BM + qr * 32 + 8 * (r / 4) + (r % 4));
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r], dqbuf, (int)lane_off,
+                                                        (int)(row * D * sizeof(float)), 0);
       }
     }
   };
 
   if (cnt > 0) {
-    load_tile(lst[0]);
+    load_tile(__builtin_amdgcn_readfirstlane(lst[0]));
     store_tile(0);
   }
 
+  // List entries are read into scalar registers: the buffer loads take the tile offset as a
+  // scalar operand.
+  int entry = cnt > 0 ? __builtin_amdgcn_readfirstlane(lst[0]) : 0;
+  int prev_qb = 0;
   for (int it = 0; it < cnt; ++it) {
-    const int entry = lst[it];
     const int qb = entry >> 1;
     const int buf = it & 1;
     const bool test = (entry & 1) || ragged_block;
+    const int next = it + 1 < cnt ? __builtin_amdgcn_readfirstlane(lst[it + 1]) : 0;
     __syncthreads();  // tile `it` staged in `buf`; dS^T of tile it-1 complete in buf ^ 1
-    if (it + 1 < cnt) load_tile(lst[it + 1]);
-    if (it > 0) dq_product(buf ^ 1, lst[it - 1] >> 1);
+    if (it + 1 < cnt) load_tile(next);
+    if (it > 0) dq_product(buf ^ 1, prev_qb);
 
     const unsigned char* qt = qdo_lds + buf * 2 * C::TILE_BYTES;
     const unsigned char* dt = qt + C::TILE_BYTES;
     const float* lse_t = rows_lds + buf * 2 * C::BM;
     const float* dlt_t = lse_t + C::BM;
 
-    // S = Q K^T and dP = dO V^T.  Register r of group g in query row block qr is tile query
-    // qr*32 + perm_index(r, g); the column is this lane's key.
-    f32x16 sacc[C::NQB], pacc[C::NQB];
+    // The tile is processed as NQB row blocks of 32 queries, one after the other, so only one
+    // block's S, dP, P and dS are live at a time.
 #pragma unroll
     for (int qr = 0; qr < C::NQB; ++qr) {
-      const int row = qr * 32 + row_source<KPL>(l32);
-      sacc[qr] = f32x16{};
-      pacc[qr] = f32x16{};
+      // S = Q K^T and dP = dO V^T for rows qr*32..: register r of group g is tile query
+      // qr*32 + perm_index(r, g); the column is this lane's key.
+      f32x16 sacc = {}, pacc = {};
+      {
+        const int row = qr * 32 + row_source<KPL>(l32);
 #pragma unroll
-      for (int s = 0; s < C::QK_STEPS; ++s) {
-        const int off = tile_off<T, 0>(row, s * KSTEP + g * KPL, C::ROW_BYTES);
-        const frag qa = *reinterpret_cast<const frag*>(qt + off);
-        const frag da = *reinterpret_cast<const frag*>(dt + off);
-        sacc[qr] = E::mfma(qa, kf[s], sacc[qr]);
-        pacc[qr] = E::mfma(da, vf[s], pacc[qr]);
+        for (int s = 0; s < C::QK_STEPS; ++s) {
+          const int off = tile_off<T, 0>(row, s * KSTEP + g * KPL, C::ROW_BYTES);
+          const frag qa = *reinterpret_cast<const frag*>(qt + off);
+          const frag da = *reinterpret_cast<const frag*>(dt + off);
+          sacc = E::mfma(qa, kf[s], sacc);
+          pacc = E::mfma(da, vf[s], pacc);
+        }
       }
-    }
 
-    // P and dS (overwriting sacc and pacc)
-#pragma unroll
-    for (int qr = 0; qr < C::NQB; ++qr)
+      // P and dS (overwriting sacc and pacc)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ql = qr * 32 + perm_index<KPL>(r, g);
-        float p = fast_exp2(fmaf(sacc[qr][r], cexp, -lse_t[ql]));
+        float p = fast_exp2(fmaf(sacc[r], cexp, -lse_t[ql]));
         if (test) {
           const int32_t q = qb * C::BM + ql;
           p = (in_stretch(q, mk.s1, mk.len1) || in_stretch(q, mk.s2, mk.len2)) ? 0.0f : p;
         }
-        sacc[qr][r] = p;
-        pacc[qr][r] = p * (pacc[qr][r] - dlt_t[ql]);
+        sacc[r] = p;
+        pacc[r] = p * (pacc[r] - dlt_t[ql]);
       }
 
-    // Operand fragments of P and dS: k-step t covers tile queries t*KSTEP + g*KPL + e,
-    // registers (t*KPL)%16 + e of query row block (t*KPL)/16.
-    frag pf[C::PQ_STEPS], sf[C::PQ_STEPS];
-#pragma unroll
-    for (int t = 0; t < C::PQ_STEPS; ++t) {
-      if constexpr (KPL == 1) {
-        pf[t] = sacc[t / 16][t % 16];
-        sf[t] = pacc[t / 16][t % 16];
-      } else {
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-          pf[t][e] = E::from_float(sacc[(t * KPL) / 16][(t * KPL) % 16 + e]);
-          sf[t][e] = E::from_float(pacc[(t * KPL) / 16][(t * KPL) % 16 + e]);
-        }
-      }
-    }
-
-    // dS^T -> LDS (key-major): this lane's key row, queries t*KSTEP + g*KPL + 0..KPL.
-    {
+      // Operand fragments of P and dS: k-step u covers tile queries
+      // qr*32 + u*KSTEP + g*KPL + e = registers u*KPL + e.
+      constexpr int US = 32 / KSTEP;
       unsigned char* dst = ds_lds + buf * C::DS_BYTES;
       const int krow = w * 32 + l32;
 #pragma unroll
-      for (int t = 0; t < C::PQ_STEPS; ++t)
-        *reinterpret_cast<frag*>(dst + tile_off<T, 1>(krow, t * KSTEP + g * KPL, C::DS_ROW_BYTES)) = sf[t];
-    }
-
-    // dV^T += dO^T P and dK^T += Q^T dS: A = rows d of the transposed tiles (contraction over
-    // the tile's queries), read with the transpose read.
+      for (int u = 0; u < US; ++u) {
+        frag pf, sf;
+        if constexpr (KPL == 1) {
+          pf = sacc[u];
+          sf = pacc[u];
+        } else {
 #pragma unroll
-    for (int t = 0; t < C::PQ_STEPS; ++t) {
+          for (int e = 0; e < KPL; ++e) {
+            pf[e] = E::from_float(sacc[u * KPL + e]);
+            sf[e] = E::from_float(pacc[u * KPL + e]);
+          }
+        }
+        const int q0 = qr * 32 + u * KSTEP;
+        // dS^T -> LDS (key-major): this lane's key row, queries q0 + g*KPL + 0..KPL.
+        *reinterpret_cast<frag*>(dst + tile_off<T, 1>(krow, q0 + g * KPL, C::DS_ROW_BYTES)) = sf;
+        // dV^T += dO^T P and dK^T += Q^T dS: A = rows d of the transposed tiles (contraction
+        // over the tile's queries q0..q0+KSTEP), read with the transpose read.
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        dv_acc[db] = E::mfma(tr_operand(dt, C::ROW_BYTES, t * KSTEP, 32 * db, SwzRow{}), pf[t], dv_acc[db]);
-        dk_acc[db] = E::mfma(tr_operand(qt, C::ROW_BYTES, t * KSTEP, 32 * db, SwzRow{}), sf[t], dk_acc[db]);
+        for (int db = 0; db < C::NDB; ++db) {
+          dv_acc[db] = E::mfma(tr_operand(dt, C::ROW_BYTES, q0, 32 * db, SwzRow{}), pf, dv_acc[db]);
+          dk_acc[db] = E::mfma(tr_operand(qt, C::ROW_BYTES, q0, 32 * db, SwzRow{}), sf, dk_acc[db]);
+        }
       }
     }
 
     // stage the next tile into the other buffer (last read in the previous iteration)
     if (it + 1 < cnt) store_tile(buf ^ 1);
+    prev_qb = qb;
+    entry = next;
   }
   if (cnt > 0) {
     __syncthreads();
-    dq_product((cnt - 1) & 1, lst[cnt - 1] >> 1);
+    dq_product((cnt - 1) & 1, prev_qb);
   }
 
   if (key_ok) {

@@ -165,16 +165,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int tr_krow = 8 * (tb >> 1) + (ti >> 2);  // + t*KSTEP (+4)
   const int tr_col = 16 * (tb & 1) + 4 * (ti & 3);  // + 32*db (elements)
 
-  if (cnt > 0) load_tile(lst[0]);
+  // List entries are read into scalar registers (the buffer loads take the tile offset as a
+  // scalar operand).
+  if (cnt > 0) load_tile(__builtin_amdgcn_readfirstlane(lst[0]));
 
   for (int it = 0; it < cnt; ++it) {
-    const int entry = lst[it];
+    const int entry = __builtin_amdgcn_readfirstlane(lst[it]);
     const int kb = entry >> 1;
     const bool test = (entry & 1) || (kb == last_kb && ragged);
     __syncthreads();  // every wave is done reading the previous tile
     store_tile(test);
     __syncthreads();
-    if (it + 1 < cnt) load_tile(lst[it + 1]);  // in flight during this tile's compute
+    if (it + 1 < cnt) load_tile(__builtin_amdgcn_readfirstlane(lst[it + 1]));
 
     // S^T = K Q^T: accumulator register r of group g in row block rb is key
     // rb*32 + perm_index(r, g) of the tile, column = this lane's query.

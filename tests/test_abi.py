@@ -93,7 +93,7 @@ def test_fwd_checks(lib):
     assert fwd(lib, shape(dtype=5)) == FM_ERR_DTYPE
     assert fwd(lib, shape(d=64)) == FM_ERR_UNSUPPORTED
     assert fwd(lib, shape(dtype=1, d=128)) == FM_ERR_UNSUPPORTED
-    for bad in (dict(B=0), dict(H=0), dict(nq=0), dict(nk=0), dict(nq=-5), dict(nk=(1 << 24) + 1)):
+    for bad in (dict(B=0), dict(H=0), dict(nq=0), dict(nk=0), dict(nq=-5), dict(nk=(1 << 22) + 1)):
         assert fwd(lib, shape(**bad)) == FM_ERR_SHAPE, bad
     assert fwd(lib, s, q=NUL) == FM_ERR_NULL
     assert fwd(lib, s, vec=NUL) == FM_ERR_NULL
