@@ -71,7 +71,7 @@ FwdWs fwd_layout(const Geometry& g) {
 }
 
 struct BwdWs {
-  size_t mm, kcnt, klist, delta, dq_acc, total;
+  size_t mm, kcnt, klist, delta, lse2, dq_acc, total;
 };
 BwdWs bwd_layout(const fm_shape* s, const Geometry& g) {
   BwdWs w;
@@ -80,7 +80,8 @@ BwdWs bwd_layout(const fm_shape* s, const Geometry& g) {
   w.kcnt = w.mm + round_up(sizeof(int32_t) * 8 * g.n_kb);
   w.klist = w.kcnt + round_up(sizeof(int32_t) * g.n_kb);
   w.delta = w.klist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb);
-  w.dq_acc = w.delta + round_up(sizeof(float) * rows);
+  w.lse2 = w.delta + round_up(sizeof(float) * rows);
+  w.dq_acc = w.lse2 + round_up(sizeof(float) * rows);
   w.total = w.dq_acc + round_up(sizeof(float) * rows * s->d);
   return w;
 }
@@ -204,6 +205,7 @@ int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const voi
   int32_t* kcnt = reinterpret_cast<int32_t*>(base + L.kcnt);
   int32_t* klist = reinterpret_cast<int32_t*>(base + L.klist);
   float* delta = reinterpret_cast<float*>(base + L.delta);
+  float* lse2 = reinterpret_cast<float*>(base + L.lse2);
   float* dq_acc = reinterpret_cast<float*>(base + L.dq_acc);
   const fm::MaskVecs mv{LTS, LTE, UTS, UTE};
 
@@ -212,8 +214,8 @@ int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const voi
     e = fm::launch_classify(mm, (int32_t)g.n_kb, s->nq, t.bm_bwd, nullptr, nullptr, nullptr, kcnt,
                             klist, hs);
   if (e == hipSuccess) {
-    fm::BwdArgs a{Q,  K,  V,      O,     dO,    LSE,  mv,           dQ,    dK,    dV,
-                  dq_acc, delta, kcnt, klist, (int32_t)g.n_qb, s->B, s->H, s->nq, s->nk, scale};
+    fm::BwdArgs a{Q,     K,    V,    O,     dO,    LSE,   mv,   dQ, dK, dV, dq_acc, delta, lse2,
+                  kcnt, klist, (int32_t)g.n_qb, s->B, s->H, s->nq, s->nk, scale};
     e = fm::launch_attn_bwd(s->dtype, a, hs, g_bwd_begin, g_bwd_end);
   }
   return hip_status(e);

@@ -82,10 +82,7 @@ __device__ inline int tile_off(int row, int col, int row_bytes) {
 }
 
 struct MaskRegs {
-  int32_t s1;
-  uint32_t len1;
-  int32_t s2;
-  uint32_t len2;
+  int32_t lts, lte, uts, ute;
 };
 
 template <typename T, int D>
@@ -105,7 +102,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   float* rows_lds = reinterpret_cast<float*>(k_lds + C::K_BYTES);       // [2][LSE2 | D]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
 
   const int n_kb = (a.nk + C::BN - 1) / C::BN;
   const int bh = blockIdx.x / n_kb;
@@ -117,7 +115,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   const T* __restrict__ dOp = static_cast<const T*>(a.dout) + (size_t)bh * a.nq * D;
   const T* __restrict__ Kp = static_cast<const T*>(a.k) + (size_t)bh * a.nk * D;
   const T* __restrict__ Vp = static_cast<const T*>(a.v) + (size_t)bh * a.nk * D;
-  const float* __restrict__ lse = a.lse + (size_t)bh * a.nq;
+  const float* __restrict__ lse2 = a.lse2 + (size_t)bh * a.nq;
   const float* __restrict__ dlt = a.delta + (size_t)bh * a.nq;
   float* __restrict__ dqa = a.dq_acc + (size_t)bh * a.nq * D;
   // dQ accumulator rows past nq fall outside this buffer, so their atomics are dropped.
@@ -126,6 +124,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   const buf_rsrc dobuf = make_buf(dOp, (uint32_t)a.nq * C::ROW_BYTES);
   const buf_rsrc kbuf = make_buf(Kp, (uint32_t)a.nk * C::ROW_BYTES);
   const buf_rsrc vbuf = make_buf(Vp, (uint32_t)a.nk * C::ROW_BYTES);
+  const buf_rsrc lbuf = make_buf(lse2, (uint32_t)a.nq * sizeof(float));
+  const buf_rsrc dlbuf = make_buf(dlt, (uint32_t)a.nq * sizeof(float));
 
   // K and V rows of this lane's key as B operands (k-step s: d = s*KSTEP + g*KPL + 0..KPL).
   frag kf[C::QK_STEPS], vf[C::QK_STEPS];
@@ -140,46 +140,63 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
       vf[s] = __builtin_bit_cast(frag, buf_load4(vbuf, off, 0));
     }
   }
-  MaskRegs mk;
-  if (key_ok) {
-    const int32_t lts = a.mask.lts[key], lte = a.mask.lte[key];
-    const int32_t uts = a.mask.uts[key], ute = a.mask.ute[key];
-    mk = {lts, stretch_len(lts, lte), uts, stretch_len(uts, ute)};
-  } else {
-    mk = {INT32_MIN, 0xffffffffu, 0, 0u};  // past the last key: masked for every row
-  }
+  MaskRegs mk = {0, 0, 0, 0};  // this lane's key; past the last key every row is masked
+  if (key_ok) mk = {a.mask.lts[key], a.mask.lte[key], a.mask.uts[key], a.mask.ute[key]};
   const bool ragged_block = (kb == n_kb - 1) && (a.nk % C::BN) != 0;
 
   // staging map: chunk c of a 256-byte row; rows 4*rq + i
   const int c = tid % C::CPR;
   const int rq = tid / C::CPR;
 
-  // transpose-read lane geometry: lane i of 16-lane block b addresses row k0 + 8*(b/2) + i/4,
+  // ---- per-lane LDS byte offsets, constant for the whole kernel ------------------------------
+  // Transpose-read lane geometry: lane i of 16-lane block b addresses row k0 + 8*(b/2) + i/4,
   // column m0 + 16*(b%2) + 4*(i%4), and receives rows k0 + 8*(l/32) + 0..3 of column m0 + l%32.
+  // The swizzles depend only on row & 15 (swz_row) or row bits 1..3 (swz_ds), so an offset
+  // computed for a row below 16 stays valid when a multiple of 16 rows is added as a constant;
+  // every LDS access below is then one of these registers plus an immediate.
   const int tb = lane >> 4, ti = lane & 15;
   const int tr_row = 8 * (tb >> 1) + (ti >> 2);
   const int tr_col = 16 * (tb & 1) + 4 * (ti & 3);
+  const int wave_db = (w * C::NOB) / C::NQB;  // the d block this wave produces in dQ
+  const int krow = w * 32 + l32;              // this lane's key row of dS^T
+  constexpr int US = 32 / KSTEP;              // k-steps in a 32-query half
 
-  // Operand of a contraction over the rows of a row-major tile (k = tile row, m = tile column):
-  // k-step rows k0..k0+KSTEP-1, columns m0..m0+31 -> lane (m = m0 + l%32, g) receives rows
-  // k0 + g*KPL + 0..KPL-1 of its column.
-  auto tr_operand = [&](const unsigned char* tile, int row_bytes, int k0, int m0,
-                        auto swz_kind) -> frag {
-    constexpr int SK = decltype(swz_kind)::value;
+  int off_s[C::QK_STEPS];  // S / dP operand (query row source row, k-step s) of a half
+  int off_tq[C::NDB][2];   // Q^T / dO^T operand rows (tr_row, tr_row + 4), columns 32*db
+  int off_dsr[C::NQB][2];  // dS^T operand rows (tr_row, tr_row + 4), columns 32*qr
+  int off_k[2];            // K operand rows (tr_row, tr_row + 4), columns 32*wave_db
+  {
+    const int srow = row_source<KPL>(l32);
+#pragma unroll
+    for (int st = 0; st < C::QK_STEPS; ++st)
+      off_s[st] = tile_off<T, 0>(srow, st * KSTEP + g * KPL, C::ROW_BYTES);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = KPL == 8 ? tr_row + 4 * h : g;
+      const int cc = KPL == 8 ? tr_col : l32;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) off_tq[db][h] = tile_off<T, 0>(r, 32 * db + cc, C::ROW_BYTES);
+#pragma unroll
+      for (int qr = 0; qr < C::NQB; ++qr) off_dsr[qr][h] = tile_off<T, 1>(r, 32 * qr + cc, C::DS_ROW_BYTES);
+      off_k[h] = tile_off<T, 0>(r, 32 * wave_db + cc, C::ROW_BYTES);
+    }
+  }
+
+  // Operand of a contraction over the rows of a row-major tile (k = tile row): rows
+  // k0 + g*KPL + 0..KPL-1 of this lane's column; `off` = {row tr_row, row tr_row + 4} offsets.
+  auto tr_operand = [&](const unsigned char* tile, const int* off, int k0_bytes) -> frag {
     if constexpr (KPL == 8) {
-      const int r = k0 + tr_row, col = m0 + tr_col;
-      const s16x4 lo = lds_read_tr16(tile + tile_off<T, SK>(r, col, row_bytes));
-      const s16x4 hi = lds_read_tr16(tile + tile_off<T, SK>(r + 4, col, row_bytes));
+      const s16x4 lo = lds_read_tr16(tile + off[0] + k0_bytes);
+      const s16x4 hi = lds_read_tr16(tile + off[1] + k0_bytes);
       return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     } else {
-      return *reinterpret_cast<const T*>(tile + tile_off<T, SK>(k0 + g, m0 + l32, row_bytes));
+      return *reinterpret_cast<const T*>(tile + off[0] + k0_bytes);
     }
   };
 
-  // The d block this wave produces in dQ.  The block's K rows are the B operand of
-  // dQ += dS K (k = the block's keys, n = d): read by transpose reads from LDS (bf16), or read
-  // once into registers through the first (Q, dO) buffer (fp32).
-  const int wave_db = (w * C::NOB) / C::NQB;
+  // The block's K rows are the B operand of dQ += dS K (k = the block's keys, n = d): read by
+  // transpose reads from LDS (bf16), or read once into registers through the first (Q, dO)
+  // buffer (fp32).
   unsigned char* kstage = C::K_IN_LDS ? k_lds : qdo_lds;
 #pragma unroll
   for (int i = 0; i < C::BN / 16; ++i) {
@@ -191,8 +208,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   if constexpr (!C::K_IN_LDS) {
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < C::DQ_STEPS; ++t)
-      kq[t] = tr_operand(kstage, C::ROW_BYTES, t * KSTEP, 32 * wave_db, SwzRow{});
+    for (int t = 0; t < C::DQ_STEPS; ++t) kq[t] = tr_operand(kstage, off_k, t * KSTEP * C::ROW_BYTES);
     __syncthreads();
   }
 
@@ -207,48 +223,38 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   const int32_t* __restrict__ lst = a.klist + (size_t)kb * a.list_stride;
   const float cexp = a.scale * kLog2e;
 
-  uint4 qreg[4], doreg[4];
-  float lse_r = INFINITY, dlt_r = 0.0f;
-  auto load_tile = [&](int entry) {
+  // Stage tile `entry` into buffer `buf` with loads straight into LDS: the tile's 64 rows of Q
+  // (then dO) are 16 blocks of 1 KiB; wave w fills blocks 4w..4w+3, lane l the 16-byte slot l
+  // of a block, i.e. row 4j + l/16, physical chunk l%16, which holds logical chunk
+  // (l%16) ^ swz_row(row).  Rows past nq read as zeros.  Waves 0 and 1 also copy the tile's
+  // LSE2 and D rows.
+  auto issue_tile = [&](int entry, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    unsigned char* qt = qdo_lds + buf * 2 * C::TILE_BYTES;
     const uint32_t tile_base = (uint32_t)(entry >> 1) * C::BM * C::ROW_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t off = (uint32_t)(4 * rq + i) * C::ROW_BYTES + c * 16;
-      qreg[i] = buf_load16(qbuf, off, tile_base);
-      doreg[i] = buf_load16(dobuf, off, tile_base);
+      const int j = 4 * w + i;
+      const int row = 4 * j + (lane >> 4);
+      const uint32_t voff = (uint32_t)row * C::ROW_BYTES + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
+      buf_load_lds<16>(qbuf, qt + j * 1024, voff, tile_base);
+      buf_load_lds<16>(dobuf, qt + C::TILE_BYTES + j * 1024, voff, tile_base);
     }
-    if (tid < C::BM) {
-      const int r = (entry >> 1) * C::BM + tid;
-      if (r < a.nq) {
-        const float x = lse[r];
-        // a fully masked row (LSE = -inf) must give P = 0: exp2(s - inf) = 0
-        lse_r = x == -INFINITY ? INFINITY : x * kLog2e;
-        dlt_r = dlt[r];
-      } else {
-        lse_r = INFINITY;
-        dlt_r = 0.0f;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* qt = qdo_lds + buf * 2 * C::TILE_BYTES;
-    unsigned char* dt = qt + C::TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int off = tile_off<T, 0>(4 * rq + i, c * CH, C::ROW_BYTES);
-      *reinterpret_cast<uint4*>(qt + off) = qreg[i];
-      *reinterpret_cast<uint4*>(dt + off) = doreg[i];
-    }
-    if (tid < C::BM) {
-      rows_lds[buf * 2 * C::BM + tid] = lse_r;
-      rows_lds[buf * 2 * C::BM + C::BM + tid] = dlt_r;
+    if (w < 2) {
+      const uint32_t roff = (uint32_t)(entry >> 1) * C::BM * sizeof(float);
+      buf_load_lds<4>(w == 0 ? lbuf : dlbuf, rows_lds + buf * 2 * C::BM + w * C::BM,
+                      (uint32_t)lane * sizeof(float), roff);
     }
   };
 
   // dQ[q][d] += sum_keys dS[q][key] K[key][d] for the tile held in dS^T buffer `buf`; wave w
   // owns d columns [32*wave_db, +32) and NOB query row blocks of them.
-  auto dq_product = [&](int buf, int qb) {
+  auto dq_product = [&](auto bufc, int qb) {
+    constexpr int buf = decltype(bufc)::value;
     const unsigned char* dst = ds_lds + buf * C::DS_BYTES;
+    // acc register r: query qr*32 + acc_row(r, g) = (qr*32 + 8*(r/4) + r%4) + 4*g,
+    // d = 32*wave_db + l32: the first part is uniform (scalar offset), the rest per lane.
+    const uint32_t lane_off = (uint32_t)((4 * g * D + wave_db * 32 + l32) * sizeof(float));
 #pragma unroll
     for (int ob = 0; ob < C::NOB; ++ob) {
       const int qr = (w * C::NOB + ob) % C::NQB;
@@ -257,14 +263,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
       for (int t = 0; t < C::DQ_STEPS; ++t) {
         frag kb_op;
         if constexpr (C::K_IN_LDS)
-          kb_op = tr_operand(k_lds, C::ROW_BYTES, t * KSTEP, 32 * wave_db, SwzRow{});
+          kb_op = tr_operand(k_lds, off_k, t * KSTEP * C::ROW_BYTES);
         else
           kb_op = kq[t];
-        acc = E::mfma(tr_operand(dst, C::DS_ROW_BYTES, t * KSTEP, 32 * qr, SwzDs{}), kb_op, acc);
+        acc = E::mfma(tr_operand(dst, off_dsr[qr], t * KSTEP * C::DS_ROW_BYTES), kb_op, acc);
       }
-      // acc register r: query qr*32 + acc_row(r, g) = (qr*32 + 8*(r/4) + r%4) + 4*g,
-      // d = 32*wave_db + l32: the first part is uniform (scalar offset), the rest per lane.
-      const uint32_t lane_off = (uint32_t)((4 * g * D + wave_db * 32 + l32) * sizeof(float));
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const uint32_t row = (uint32_t)(qb * C::BM + qr * 32 + 8 * (r / 4) + (r % 4));
@@ -274,28 +277,42 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
     }
   };
 
-  if (cnt > 0) {
-    load_tile(__builtin_amdgcn_readfirstlane(lst[0]));
-    store_tile(0);
-  }
+  // Row mask of this lane's key over a tile's BM query rows starting at q0 (bit i = row q0 + i
+  // masked), pre-shifted by g*KPL so that bit qr*32 + perm_index(r, 0) belongs to register r of
+  // row block qr in this lane group.
+  auto tile_row_mask = [&](int32_t q0) -> uint64_t {
+    auto bits = [&](int32_t s0, int32_t e0) -> uint64_t {
+      const int32_t lo = s0 <= q0 ? 0 : (s0 >= q0 + 64 ? 64 : s0 - q0);
+      const int32_t hi = e0 <= q0 ? 0 : (e0 >= q0 + 64 ? 64 : e0 - q0);
+      if (hi <= lo) return 0ull;
+      const uint64_t upto_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+      return upto_hi & ~((1ull << lo) - 1ull);  // lo < 64 here
+    };
+    const uint64_t m = key_ok ? (bits(mk.lts, mk.lte) | bits(mk.uts, mk.ute)) : ~0ull;
+    return m >> (g * KPL);
+  };
 
   // List entries are read into scalar registers: the buffer loads take the tile offset as a
   // scalar operand.
   int entry = cnt > 0 ? __builtin_amdgcn_readfirstlane(lst[0]) : 0;
   int prev_qb = 0;
-  for (int it = 0; it < cnt; ++it) {
+
+  auto body = [&](const int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int qb = entry >> 1;
-    const int buf = it & 1;
     const bool test = (entry & 1) || ragged_block;
     const int next = it + 1 < cnt ? __builtin_amdgcn_readfirstlane(lst[it + 1]) : 0;
-    __syncthreads();  // tile `it` staged in `buf`; dS^T of tile it-1 complete in buf ^ 1
-    if (it + 1 < cnt) load_tile(next);
-    if (it > 0) dq_product(buf ^ 1, prev_qb);
+    wait_vmem();      // this wave's loads of tile `it` have landed in LDS
+    __syncthreads();  // ... everyone's; dS^T of tile it-1 complete in buf ^ 1
+    if (it + 1 < cnt) issue_tile(next, std::integral_constant<int, buf ^ 1>{});
+    if (it > 0) dq_product(std::integral_constant<int, buf ^ 1>{}, prev_qb);
 
     const unsigned char* qt = qdo_lds + buf * 2 * C::TILE_BYTES;
     const unsigned char* dt = qt + C::TILE_BYTES;
     const float* lse_t = rows_lds + buf * 2 * C::BM;
     const float* dlt_t = lse_t + C::BM;
+    unsigned char* dsw = ds_lds + buf * C::DS_BYTES;
+    const uint64_t mrow = test ? tile_row_mask(qb * C::BM) : 0ull;
 
     // The tile is processed as NQB row blocks of 32 queries, one after the other, so only one
     // block's S, dP, P and dS are live at a time.
@@ -304,36 +321,64 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
       // S = Q K^T and dP = dO V^T for rows qr*32..: register r of group g is tile query
       // qr*32 + perm_index(r, g); the column is this lane's key.
       f32x16 sacc = {}, pacc = {};
-      {
-        const int row = qr * 32 + row_source<KPL>(l32);
 #pragma unroll
-        for (int s = 0; s < C::QK_STEPS; ++s) {
-          const int off = tile_off<T, 0>(row, s * KSTEP + g * KPL, C::ROW_BYTES);
-          const frag qa = *reinterpret_cast<const frag*>(qt + off);
-          const frag da = *reinterpret_cast<const frag*>(dt + off);
-          sacc = E::mfma(qa, kf[s], sacc);
-          pacc = E::mfma(da, vf[s], pacc);
+      for (int st = 0; st < C::QK_STEPS; ++st) {
+        const int off = off_s[st] + qr * 32 * C::ROW_BYTES;
+        const frag qa = *reinterpret_cast<const frag*>(qt + off);
+        const frag da = *reinterpret_cast<const frag*>(dt + off);
+        sacc = E::mfma(qa, kf[st], sacc);
+        pacc = E::mfma(da, vf[st], pacc);
+      }
+
+      // LSE (log2 units) and D of the 16 queries this lane holds: runs of KPL consecutive rows
+      // qr*32 + (r/KPL)*2*KPL + g*KPL + 0..KPL-1.
+      float lsev[16], dltv[16];
+      if constexpr (KPL == 8) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int q = qr * 32 + 16 * j + 8 * g;
+          const float4 l0 = *reinterpret_cast<const float4*>(lse_t + q);
+          const float4 l1 = *reinterpret_cast<const float4*>(lse_t + q + 4);
+          const float4 d0 = *reinterpret_cast<const float4*>(dlt_t + q);
+          const float4 d1 = *reinterpret_cast<const float4*>(dlt_t + q + 4);
+          const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+          const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            lsev[8 * j + e] = lv[e];
+            dltv[8 * j + e] = dv[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          lsev[r] = lse_t[qr * 32 + perm_index<KPL>(r, g)];
+          dltv[r] = dlt_t[qr * 32 + perm_index<KPL>(r, g)];
         }
       }
 
-      // P and dS (overwriting sacc and pacc)
+      // P and dS (overwriting sacc and pacc); the masked variant is a separate code path so
+      // unmasked tiles pay nothing for the test.
+      auto elementwise = [&](auto masked_c) {
+        constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = qr * 32 + perm_index<KPL>(r, g);
-        float p = fast_exp2(fmaf(sacc[r], cexp, -lse_t[ql]));
-        if (test) {
-          const int32_t q = qb * C::BM + ql;
-          p = (in_stretch(q, mk.s1, mk.len1) || in_stretch(q, mk.s2, mk.len2)) ? 0.0f : p;
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(fmaf(sacc[r], cexp, -lsev[r]));
+          if constexpr (MASKED) {
+            const int bit = qr * 32 + perm_index<KPL>(r, 0);
+            p = ((mrow >> bit) & 1ull) ? 0.0f : p;
+          }
+          sacc[r] = p;
+          pacc[r] = p * (pacc[r] - dltv[r]);
         }
-        sacc[r] = p;
-        pacc[r] = p * (pacc[r] - dlt_t[ql]);
-      }
+      };
+      if (test)
+        elementwise(std::true_type{});
+      else
+        elementwise(std::false_type{});
 
       // Operand fragments of P and dS: k-step u covers tile queries
       // qr*32 + u*KSTEP + g*KPL + e = registers u*KPL + e.
-      constexpr int US = 32 / KSTEP;
-      unsigned char* dst = ds_lds + buf * C::DS_BYTES;
-      const int krow = w * 32 + l32;
 #pragma unroll
       for (int u = 0; u < US; ++u) {
         frag pf, sf;
@@ -349,25 +394,33 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
         }
         const int q0 = qr * 32 + u * KSTEP;
         // dS^T -> LDS (key-major): this lane's key row, queries q0 + g*KPL + 0..KPL.
-        *reinterpret_cast<frag*>(dst + tile_off<T, 1>(krow, q0 + g * KPL, C::DS_ROW_BYTES)) = sf;
+        *reinterpret_cast<frag*>(dsw + tile_off<T, 1>(krow, q0 + g * KPL, C::DS_ROW_BYTES)) = sf;
         // dV^T += dO^T P and dK^T += Q^T dS: A = rows d of the transposed tiles (contraction
         // over the tile's queries q0..q0+KSTEP), read with the transpose read.
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          dv_acc[db] = E::mfma(tr_operand(dt, C::ROW_BYTES, q0, 32 * db, SwzRow{}), pf, dv_acc[db]);
-          dk_acc[db] = E::mfma(tr_operand(qt, C::ROW_BYTES, q0, 32 * db, SwzRow{}), sf, dk_acc[db]);
+          dv_acc[db] = E::mfma(tr_operand(dt, off_tq[db], q0 * C::ROW_BYTES), pf, dv_acc[db]);
+          dk_acc[db] = E::mfma(tr_operand(qt, off_tq[db], q0 * C::ROW_BYTES), sf, dk_acc[db]);
         }
       }
     }
 
-    // stage the next tile into the other buffer (last read in the previous iteration)
-    if (it + 1 < cnt) store_tile(buf ^ 1);
     prev_qb = qb;
     entry = next;
+  };
+
+  if (cnt > 0) issue_tile(entry, std::integral_constant<int, 0>{});
+  // Unrolled by two so each buffer index is a compile-time constant.
+  for (int it = 0; it < cnt; it += 2) {
+    body(it, std::integral_constant<int, 0>{});
+    if (it + 1 < cnt) body(it + 1, std::integral_constant<int, 1>{});
   }
   if (cnt > 0) {
     __syncthreads();
-    dq_product((cnt - 1) & 1, prev_qb);
+    if ((cnt - 1) & 1)
+      dq_product(std::integral_constant<int, 1>{}, prev_qb);
+    else
+      dq_product(std::integral_constant<int, 0>{}, prev_qb);
   }
 
   if (key_ok) {
@@ -398,12 +451,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   }
 }
 
-// D_i = sum_d dO_id O_id (float32) and the dQ accumulator row cleared.  16 threads per row,
-// one 16-byte chunk of O and dO each.
+// D_i = sum_d dO_id O_id (float32), LSE_i * log2(e) (+inf for fully masked rows) and the dQ
+// accumulator row cleared.  16 threads per row, one 16-byte chunk of O and dO each.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
                                                       const T* __restrict__ dout,
+                                                      const float* __restrict__ lse,
                                                       float* __restrict__ delta,
+                                                      float* __restrict__ lse2,
                                                       float* __restrict__ dq_acc, int64_t rows) {
   constexpr int CH = 16 / (int)sizeof(T);
   static_assert(D / CH == 16, "16 chunks per row");
@@ -419,7 +474,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
   for (int e = 0; e < CH; ++e) acc = fmaf((float)eo[e], (float)ed[e], acc);
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (c == 0) delta[row] = acc;
+  if (c == 0) {
+    delta[row] = acc;
+    // LSE in log2 units; a fully masked row (LSE = -inf) gets +inf so that exp2(s - lse2) = 0
+    const float x = lse[row];
+    lse2[row] = x == -INFINITY ? INFINITY : x * kLog2e;
+  }
   float4* z = reinterpret_cast<float4*>(dq_acc + row * D);
   constexpr int per = D / 4 / 16;  // float4 stores per thread
 #pragma unroll
@@ -455,8 +515,8 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin, hi
   const int64_t rows = (int64_t)a.B * a.H * a.nq;
   const int pre_grid = (int)((rows + 15) / 16);
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, stream,
-                     static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.delta, a.dq_acc,
-                     rows);
+                     static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.delta,
+                     a.lse2, a.dq_acc, rows);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 

@@ -111,6 +111,23 @@ __device__ inline uint32_t buf_load4(buf_rsrc r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
+// Buffer load straight into LDS (no registers): lane l's `bytes` (4 or 16) land at
+// lds_base + l * bytes, where lds_base must be the same for the whole wave; lanes whose offset
+// is out of range write zeros.
+template <int BYTES>
+__device__ inline void buf_load_lds(buf_rsrc r, void* lds_base, uint32_t voff, uint32_t soff) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  if constexpr (BYTES == 16) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_base), 16, voff, soff, 0, 0);
+  } else {
+    static_assert(BYTES == 4, "4 or 16 bytes per lane");
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_base), 4, voff, soff, 0, 0);
+  }
+}
+// Wait until this wave's outstanding vector-memory operations (including loads into LDS) are
+// complete: s_waitcnt vmcnt(0), other counters left alone.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 // ---- LDS transpose read (gfx950 ds_read_b64_tr_b16) ------------------------------------------
 // Within each block of 16 lanes, lane i receives element i%4 of the four 16-bit elements that
 // lane 4*j + i/4 addressed, for j = 0..3.  So if lane i addresses X[k0 + i/4][m0 + 4*(i%4)] of a

@@ -66,6 +66,7 @@ struct BwdArgs {
   void* dv;
   float* dq_acc;  // float32 [B,H,nq,d]
   float* delta;   // float32 [B,H,nq]
+  float* lse2;    // float32 [B,H,nq]: LSE * log2(e), +inf on fully masked rows
   const int32_t* kcnt;
   const int32_t* klist;
   int32_t list_stride;  // n_qb

@@ -75,7 +75,7 @@ def test_workspace_sizes(lib):
     assert lib.flashmask_fwd_workspace_bytes(ctypes.byref(s)) == r(32 * n_kb) + r(4 * n_qb) + r(4 * n_qb * n_kb)
     n_qb, n_kb = 5, 2      # backward tiles 64 x 128
     rows = 1 * 2 * 300
-    want = r(32 * n_kb) + r(4 * n_kb) + r(4 * n_qb * n_kb) + r(4 * rows) + r(4 * rows * 128)
+    want = r(32 * n_kb) + r(4 * n_kb) + r(4 * n_qb * n_kb) + 2 * r(4 * rows) + r(4 * rows * 128)
     assert lib.flashmask_bwd_workspace_bytes(ctypes.byref(s)) == want
     assert lib.flashmask_fwd_workspace_bytes(ctypes.byref(shape(d=64))) == 0
     assert lib.flashmask_classify_workspace_bytes(1000, 64) == 512
