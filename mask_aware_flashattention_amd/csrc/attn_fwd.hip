@@ -71,10 +71,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
 
   const int n_qb = (a.nq + C::BM - 1) / C::BM;
-  const int bh = blockIdx.x / n_qb;
+  const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
+  const int bh = work / n_qb;
   // Query blocks are visited last-first: under causal-like masks the later blocks have the
   // longest lists, so the longest work is dispatched first.
-  const int qb = n_qb - 1 - (int)(blockIdx.x % n_qb);
+  const int qb = n_qb - 1 - (work % n_qb);
 
   const T* __restrict__ Qp = static_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
   const T* __restrict__ Kp = static_cast<const T*>(a.k) + (size_t)bh * a.nk * D;

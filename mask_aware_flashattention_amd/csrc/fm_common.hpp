@@ -96,6 +96,18 @@ __host__ __device__ inline uint32_t stretch_len(int32_t s, int32_t e) {
   return e > s ? (uint32_t)e - (uint32_t)s : 0u;
 }
 
+// ---- XCD-aware work order ---------------------------------------------------------------------
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i to XCD i % 8), each with
+// its own L2.  This maps the dispatch index to a work index so that every XCD walks one
+// contiguous range of the work list: neighbouring work items (query or key blocks of the same
+// head, which read the same K/V or Q/dO rows) then share an L2.
+constexpr int kNumXcd = 8;
+__device__ inline int xcd_contiguous_index(int bid, int nwg) {
+  const int xcd = bid % kNumXcd, slot = bid / kNumXcd;
+  const int q = nwg / kNumXcd, r = nwg % kNumXcd;
+  return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
 // ---- raw buffer loads: out-of-range offsets return zeros, so tails need no branches ----------
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 
