@@ -26,8 +26,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 METRIC = "achieved TFLOP/s (unmasked FLOPs) fwd & bwd, % of bf16 MFMA peak, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_c3_hbm_traffic.txt")
-KERNEL_SOURCES = ["attn_bwd.hip", "fm_common.hpp", "launch.hpp"]
+TRAFFIC_FILES = {"bwd": os.path.join(ROOT, "profiles", "attn_bwd_c3_hbm_traffic.txt"),
+                 "fwd": os.path.join(ROOT, "profiles", "attn_fwd_c3_hbm_traffic.txt")}
+KERNEL_SOURCES = {"bwd": ["attn_bwd.hip", "fm_common.hpp", "launch.hpp"],
+                  "fwd": ["attn_fwd.hip", "fm_common.hpp", "launch.hpp"]}
 
 
 def unmasked_entries(vectors, nq: int) -> int:
@@ -42,24 +44,26 @@ def unmasked_entries(vectors, nq: int) -> int:
     return int(nq * len(a1) - (l1 + l2 - ov).sum())
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(which: str = "bwd") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[which]:
         with open(os.path.join(ROOT, "mask_aware_flashattention_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(launch_units: int):
-    """HBM bytes per launch of the backward kernel from the committed counter summary, or None
-    if it is missing or was taken on different kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+def load_traffic(which: str):
+    """HBM bytes per launch of the forward or backward attention kernel at the n=32768 workload,
+    from the committed counter summary, or None if it is missing or was taken on different
+    kernel sources."""
+    path = TRAFFIC_FILES[which]
+    if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
     except ValueError:
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(which):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -215,7 +219,9 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = (flop_f + flop_b) / (ms_per_step * 1e-3) / 1e12
 
-    traffic = load_traffic(1)
+    on_c3 = w.key == "c3"
+    traffic = load_traffic("bwd") if on_c3 else None
+    traffic_f = load_traffic("fwd") if on_c3 else None
     bwd_achieved = flop_b / (bwd_kernel_ms * 1e-3) / 1e12
     out = {
         "metric": METRIC,
@@ -247,7 +253,8 @@ def main():
         "roofline_fwd": {"kernel": "attn_fwd_kernel<bf16,128>", "bound": "mfma",
                          "achieved": round(flop_f / (fwd_kernel_ms * 1e-3) / 1e12, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(flop_f / (fwd_kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+                         "frac": round(flop_f / (fwd_kernel_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "traffic": traffic_f},
     }
     if not args.no_cpu_baseline:
         # the oracle takes the global vectors with the global row number of every local row
