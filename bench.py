@@ -28,7 +28,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "achieved TFLOP/s (unmasked FLOPs) fwd & bwd, % of bf16 MFMA peak, 1 GPU"
 TRAFFIC_FILES = {"bwd": os.path.join(ROOT, "profiles", "attn_bwd_c3_hbm_traffic.txt"),
                  "fwd": os.path.join(ROOT, "profiles", "attn_fwd_c3_hbm_traffic.txt")}
-KERNEL_SOURCES = {"bwd": ["attn_bwd.hip", "fm_common.hpp", "launch.hpp"],
+KERNEL_SOURCES = {"bwd": ["attn_bwd.hip", "attn_bwd_dq.hip", "fm_common.hpp", "launch.hpp"],
                   "fwd": ["attn_fwd.hip", "fm_common.hpp", "launch.hpp"]}
 
 
@@ -53,7 +53,8 @@ def kernel_source_hash(which: str = "bwd") -> str:
 
 
 def load_traffic(which: str):
-    """HBM bytes per launch of the forward or backward attention kernel at the n=32768 workload,
+    """HBM bytes per launch of the forward attention kernel, or of the backward's two kernels
+    together, at the n=32768 workload,
     from the committed counter summary, or None if it is missing or was taken on different
     kernel sources."""
     path = TRAFFIC_FILES[which]
@@ -246,7 +247,9 @@ def main():
         "bwd": {"call_ms": round(bwd_call_ms, 4), "kernel_ms": round(bwd_kernel_ms, 4),
                 "tflops_call": round(flop_b / bwd_call_ms / 1e9, 2),
                 "frac_of_peak_call": round(flop_b / bwd_call_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
-        "roofline": {"kernel": "attn_bwd_kernel<bf16,128>", "bound": "mfma",
+        # the backward's two kernels (dK/dV, then dQ) run back to back and are timed as one span
+        "roofline": {"kernel": "attn_bwd_kernel<bf16,128> + attn_dq_kernel<bf16,128>",
+                     "bound": "mfma",
                      "achieved": round(bwd_achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bwd_achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},

@@ -96,9 +96,12 @@ int32_t flashmask_fwd(const fm_shape* shape, const void* Q, const void* K, const
  *   P = exp(S - LSE) (0 where masked), dP = dO V^T, D_i = sum_d dO_id O_id,
  *   dS = P * (dP - D), dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K.
  * O and LSE are the forward's outputs.  Rows with LSE = -inf contribute nothing; their dQ is 0.
- * dQ [B,H,nq,d], dK/dV [B,H,nk,d] in `dtype`, overwritten.  dQ is accumulated in float32 with
- * atomics inside the call, so its last bits may differ between runs; dK and dV are
+ * dQ [B,H,nq,d], dK/dV [B,H,nk,d] in `dtype`, overwritten.  dK and dV come from a kernel that
+ * holds a key block and walks its query blocks, dQ from one that holds a query block and walks
+ * its key blocks (both skip fully masked tiles); no atomics are used and all three results are
  * deterministic.
+ * ws: device workspace of at least flashmask_bwd_workspace_bytes(shape) bytes (256-byte
+ * aligned slabs: tile lists at both tile shapes, and float32 D and LSE*log2(e) per row).
  */
 size_t flashmask_bwd_workspace_bytes(const fm_shape* shape);
 int32_t flashmask_bwd(const fm_shape* shape, const void* Q, const void* K, const void* V,

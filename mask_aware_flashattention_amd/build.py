@@ -19,11 +19,13 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libflashmask.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "mask_kernels.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["api.cpp", "mask_kernels.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"]
+# Per-source code-generation options (none at present).
+EXTRA = {}
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics", "-I", os.path.join(ROOT, "include")]
+          "-I", os.path.join(ROOT, "include")]
 
 
 def _hipcc():
@@ -35,7 +37,7 @@ def _hipcc():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -13,8 +13,8 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxListEntries = (int64_t(1) << 31) - 1;
-// Per (batch, head) every slab the kernels address with 32-bit buffer offsets (Q, K, V, O and
-// the float32 dQ accumulator, at most 512 bytes per row) must stay below 4 GiB.
+// Per (batch, head) every slab the kernels address with 32-bit buffer offsets (Q, K, V, O, dO;
+// 256 bytes per row) must stay below 4 GiB.
 constexpr int32_t kMaxLen = int32_t(1) << 22;
 
 inline size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -70,19 +70,23 @@ FwdWs fwd_layout(const Geometry& g) {
   return w;
 }
 
+// Backward workspace: key-block lists at the backward tile shape (dK/dV kernel), query-block
+// lists at the forward tile shape (dQ kernel), and the per-row D and LSE * log2(e).
 struct BwdWs {
-  size_t mm, kcnt, klist, delta, lse2, dq_acc, total;
+  size_t mm, kcnt, klist, mm_f, qcnt, qlist, delta, lse2, total;
 };
-BwdWs bwd_layout(const fm_shape* s, const Geometry& g) {
+BwdWs bwd_layout(const fm_shape* s, const Geometry& g, const Geometry& gf) {
   BwdWs w;
   const size_t rows = size_t(s->B) * s->H * s->nq;
   w.mm = 0;
   w.kcnt = w.mm + round_up(sizeof(int32_t) * 8 * g.n_kb);
   w.klist = w.kcnt + round_up(sizeof(int32_t) * g.n_kb);
-  w.delta = w.klist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb);
+  w.mm_f = w.klist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb);
+  w.qcnt = w.mm_f + round_up(sizeof(int32_t) * 8 * gf.n_kb);
+  w.qlist = w.qcnt + round_up(sizeof(int32_t) * gf.n_qb);
+  w.delta = w.qlist + round_up(sizeof(int32_t) * gf.n_qb * gf.n_kb);
   w.lse2 = w.delta + round_up(sizeof(float) * rows);
-  w.dq_acc = w.lse2 + round_up(sizeof(float) * rows);
-  w.total = w.dq_acc + round_up(sizeof(float) * rows * s->d);
+  w.total = w.lse2 + round_up(sizeof(float) * rows);
   return w;
 }
 
@@ -173,9 +177,10 @@ int32_t flashmask_fwd(const fm_shape* s, const void* Q, const void* K, const voi
 size_t flashmask_bwd_workspace_bytes(const fm_shape* s) {
   if (!s || check_dtype(s->dtype, s->d) != FM_OK) return 0;
   const fm::TileShape t = tiles(s->dtype);
-  Geometry g;
+  Geometry g, gf;
   if (check_shape(s, t.bm_bwd, t.bn_bwd, &g) != FM_OK) return 0;
-  return bwd_layout(s, g).total;
+  if (check_shape(s, t.bm_fwd, t.bn_fwd, &gf) != FM_OK) return 0;
+  return bwd_layout(s, g, gf).total;
 }
 
 int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const void* V,
@@ -186,8 +191,9 @@ int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const voi
   int32_t st = check_dtype(s->dtype, s->d);
   if (st != FM_OK) return st;
   const fm::TileShape t = tiles(s->dtype);
-  Geometry g;
+  Geometry g, gf;
   if ((st = check_shape(s, t.bm_bwd, t.bn_bwd, &g)) != FM_OK) return st;
+  if ((st = check_shape(s, t.bm_fwd, t.bn_fwd, &gf)) != FM_OK) return st;
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FM_ERR_NULL;
   if ((st = check_vectors(LTS, LTE, UTS, UTE)) != FM_OK) return st;
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
@@ -195,7 +201,7 @@ int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const voi
       !aligned(LSE, 4))
     return FM_ERR_ALIGN;
   if ((st = check_scale(scale)) != FM_OK) return st;
-  const BwdWs L = bwd_layout(s, g);
+  const BwdWs L = bwd_layout(s, g, gf);
   if (!ws || ws_bytes < L.total) return FM_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return FM_ERR_ALIGN;
 
@@ -204,19 +210,30 @@ int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const voi
   int32_t* mm = reinterpret_cast<int32_t*>(base + L.mm);
   int32_t* kcnt = reinterpret_cast<int32_t*>(base + L.kcnt);
   int32_t* klist = reinterpret_cast<int32_t*>(base + L.klist);
+  int32_t* mm_f = reinterpret_cast<int32_t*>(base + L.mm_f);
+  int32_t* qcnt = reinterpret_cast<int32_t*>(base + L.qcnt);
+  int32_t* qlist = reinterpret_cast<int32_t*>(base + L.qlist);
   float* delta = reinterpret_cast<float*>(base + L.delta);
   float* lse2 = reinterpret_cast<float*>(base + L.lse2);
-  float* dq_acc = reinterpret_cast<float*>(base + L.dq_acc);
   const fm::MaskVecs mv{LTS, LTE, UTS, UTE};
 
   hipError_t e = fm::launch_block_minmax(mv, s->nk, t.bn_bwd, mm, hs);
   if (e == hipSuccess)
     e = fm::launch_classify(mm, (int32_t)g.n_kb, s->nq, t.bm_bwd, nullptr, nullptr, nullptr, kcnt,
                             klist, hs);
+  if (e == hipSuccess) e = fm::launch_block_minmax(mv, s->nk, t.bn_fwd, mm_f, hs);
+  if (e == hipSuccess)
+    e = fm::launch_classify(mm_f, (int32_t)gf.n_kb, s->nq, t.bm_fwd, nullptr, qcnt, qlist, nullptr,
+                            nullptr, hs);
   if (e == hipSuccess) {
-    fm::BwdArgs a{Q,     K,    V,    O,     dO,    LSE,   mv,   dQ, dK, dV, dq_acc, delta, lse2,
-                  kcnt, klist, (int32_t)g.n_qb, s->B, s->H, s->nq, s->nk, scale};
-    e = fm::launch_attn_bwd(s->dtype, a, hs, g_bwd_begin, g_bwd_end);
+    fm::BwdArgs a{Q,     K,    V,     O,    dO,   LSE,  mv,   dK, dV, delta, lse2, kcnt, klist,
+                  (int32_t)g.n_qb, s->B, s->H, s->nq, s->nk, scale};
+    e = fm::launch_attn_bwd(s->dtype, a, hs, g_bwd_begin);
+  }
+  if (e == hipSuccess) {
+    fm::DqArgs a{Q,    K,     V,     dO,    mv,   dQ,   delta, lse2, qcnt, qlist,
+                 (int32_t)gf.n_kb, s->B, s->H, s->nq, s->nk, scale};
+    e = fm::launch_attn_dq(s->dtype, a, hs, g_bwd_end);
   }
   return hip_status(e);
 }

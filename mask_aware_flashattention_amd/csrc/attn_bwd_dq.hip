@@ -1,0 +1,292 @@
+// dQ of the mask-aware attention backward, query-stationary, without atomics.
+//
+// The pages report the backward's speed ("FlashMask-3 ..." zicq.com summary, end-to-end
+// paragraph) but do not describe it.  This kernel computes dQ = scale * dS K for one query
+// block per workgroup, walking the same list of key tiles the forward walks (fully masked tiles
+// skipped, the row test only in partly masked tiles; "FlashMask-3 sends each GPU its mask ...",
+// tile-classification paragraph), recomputing P from the saved LSE and dP from dO and V.
+// dK and dV come from the key-stationary kernel in attn_bwd.hip; splitting the two products
+// this way needs no float32 atomics and gives a deterministic dQ.
+//
+// Layout (the forward's, with dP added): one workgroup = 4 waves = 128 query rows against key
+// tiles of 64; each wave holds its 32 rows of Q and dO in registers as the B operands of
+// S^T = K Q^T and dP^T = V dO^T (K, V rows loaded in a permuted order so the accumulators are
+// already laid out as operands), forms dS^T = P^T * (dP^T - D) in registers, and accumulates
+// dQ^T += K^T dS^T with the K^T operand read by the gfx950 LDS transpose read.  K and V tiles go
+// straight from HBM into LDS (XOR-swizzled, double-buffered, one barrier per tile).
+#include <math.h>
+
+#include "fm_common.hpp"
+#include "launch.hpp"
+
+namespace fm {
+
+namespace {
+
+template <typename T, int D>
+struct DqTile {
+  static constexpr int BM = 128, BN = 64, NT = 256;
+  static constexpr int KPL = Elem<T>::KPL, KSTEP = 2 * KPL;
+  static constexpr int CH = 16 / (int)sizeof(T);
+  static constexpr int CPR = D / CH;
+  static constexpr int ROW_BYTES = D * (int)sizeof(T);
+  static constexpr int NRB = BN / 32;  // 32-key row blocks of S^T
+  static constexpr int NDB = D / 32;   // 32-wide d blocks of dQ^T
+  static constexpr int QK_STEPS = D / KSTEP;
+  static constexpr int KV_STEPS = BN / KSTEP;  // k-steps over a tile's keys
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;
+  static constexpr int MW_BYTES = 4 * BN * 4;  // per wave, per key: one 32-bit row mask
+  static_assert(CPR == 16, "256-byte rows");
+  static_assert(BN * ROW_BYTES == 16 * 1024, "16 blocks of 1 KiB per tile");
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
+  using C = DqTile<T, D>;
+  using E = Elem<T>;
+  using frag = typename E::frag;
+  constexpr int KPL = C::KPL, KSTEP = C::KSTEP;
+
+  // LDS: two (K, V) tile buffers, two mask-word buffers.
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* kv_lds = smem;                                   // [2][K | V]
+  uint32_t* mw_lds = reinterpret_cast<uint32_t*>(smem + 4 * C::TILE_BYTES);  // [2][4][BN]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int n_qb = (a.nq + C::BM - 1) / C::BM;
+  const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
+  const int bh = work / n_qb;
+  const int qb = n_qb - 1 - (work % n_qb);
+
+  const T* __restrict__ Qp = static_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
+  const T* __restrict__ dOp = static_cast<const T*>(a.dout) + (size_t)bh * a.nq * D;
+  const T* __restrict__ Kp = static_cast<const T*>(a.k) + (size_t)bh * a.nk * D;
+  const T* __restrict__ Vp = static_cast<const T*>(a.v) + (size_t)bh * a.nk * D;
+  const buf_rsrc qbuf = make_buf(Qp, (uint32_t)a.nq * C::ROW_BYTES);
+  const buf_rsrc dobuf = make_buf(dOp, (uint32_t)a.nq * C::ROW_BYTES);
+  const buf_rsrc kbuf = make_buf(Kp, (uint32_t)a.nk * C::ROW_BYTES);
+  const buf_rsrc vbuf = make_buf(Vp, (uint32_t)a.nk * C::ROW_BYTES);
+
+  const int q0w = qb * C::BM + w * 32;  // first query row of this wave
+  const int q_row = q0w + l32;          // this lane's query row
+  const bool row_ok = q_row < a.nq;
+
+  // Q and dO rows of this lane's query as B operands (k-step s: d = s*KSTEP + g*KPL + 0..KPL);
+  // rows past nq read as zeros.
+  frag qf[C::QK_STEPS], dof[C::QK_STEPS];
+#pragma unroll
+  for (int s = 0; s < C::QK_STEPS; ++s) {
+    const uint32_t off = (uint32_t)q_row * C::ROW_BYTES + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
+    if constexpr (KPL == 8) {
+      qf[s] = __builtin_bit_cast(frag, buf_load16(qbuf, off, 0));
+      dof[s] = __builtin_bit_cast(frag, buf_load16(dobuf, off, 0));
+    } else {
+      qf[s] = __builtin_bit_cast(frag, buf_load4(qbuf, off, 0));
+      dof[s] = __builtin_bit_cast(frag, buf_load4(dobuf, off, 0));
+    }
+  }
+  // this row's LSE (log2 units, +inf when fully masked) and D
+  const float lse2 = row_ok ? a.lse2[(size_t)bh * a.nq + q_row] : INFINITY;
+  const float dlt = row_ok ? a.delta[(size_t)bh * a.nq + q_row] : 0.0f;
+
+  const int cnt = a.qcnt[qb];
+  const int32_t* __restrict__ lst = a.qlist + (size_t)qb * a.list_stride;
+  const int last_kb = (a.nk - 1) / C::BN;
+  const bool ragged = (a.nk % C::BN) != 0;
+  const float cexp = a.scale * kLog2e;
+
+  // per-lane LDS byte offsets (see attn_bwd.hip: swizzles depend on row & 15 only)
+  const int tb = lane >> 4, ti = lane & 15;
+  const int tr_row = 8 * (tb >> 1) + (ti >> 2);
+  const int tr_col = 16 * (tb & 1) + 4 * (ti & 3);
+  int off_s[C::QK_STEPS];  // K / V row operand (permuted row source, k-step s) of a 32-key block
+  int off_tk[C::NDB][2];   // K^T operand rows (tr_row, tr_row + 4), columns 32*db
+  {
+    const int srow = row_source<KPL>(l32);
+#pragma unroll
+    for (int st = 0; st < C::QK_STEPS; ++st)
+      off_s[st] = tile_off<T, 0>(srow, st * KSTEP + g * KPL, C::ROW_BYTES);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+        off_tk[db][h] = KPL == 8 ? tile_off<T, 0>(tr_row + 4 * h, 32 * db + tr_col, C::ROW_BYTES)
+                                 : tile_off<T, 0>(g, 32 * db + l32, C::ROW_BYTES);
+  }
+  auto tr_operand = [&](const unsigned char* tile, const int* off, int k0_bytes) -> frag {
+    if constexpr (KPL == 8) {
+      const s16x4 lo = lds_read_tr16(tile + off[0] + k0_bytes);
+      const s16x4 hi = lds_read_tr16(tile + off[1] + k0_bytes);
+      return __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return *reinterpret_cast<const T*>(tile + off[0] + k0_bytes);
+    }
+  };
+
+  // Stage key tile `entry` into buffer `buf`: K then V, 16 blocks of 1 KiB each, wave w fills
+  // blocks 4w..4w+3 (lane l: row 4j + l/16, physical chunk l%16 = logical chunk
+  // (l%16) ^ swz_row(row)); keys past nk read as zeros.  In partly masked tiles thread tid
+  // also writes the row mask of key tid%64 for wave tid/64's 32 rows.
+  auto issue_tile = [&](int entry, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int kb = entry >> 1;
+    unsigned char* kt = kv_lds + buf * 2 * C::TILE_BYTES;
+    const uint32_t tile_base = (uint32_t)kb * C::BN * C::ROW_BYTES;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * w + i;
+      const int row = 4 * j + (lane >> 4);
+      const uint32_t voff = (uint32_t)row * C::ROW_BYTES + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
+      buf_load_lds<16>(kbuf, kt + j * 1024, voff, tile_base);
+      buf_load_lds<16>(vbuf, kt + C::TILE_BYTES + j * 1024, voff, tile_base);
+    }
+    const bool test = (entry & 1) || (kb == last_kb && ragged);
+    if (test) {
+      const int mkey = lane;  // key of the tile; the word is for this wave's rows
+      const int jk = kb * C::BN + mkey;
+      uint32_t word = 0xffffffffu;  // past the last key: masked for every row
+      if (jk < a.nk) {
+        auto bits = [&](int32_t s0, int32_t e0) -> uint32_t {
+          const int32_t lo = s0 <= q0w ? 0 : (s0 >= q0w + 32 ? 32 : s0 - q0w);
+          const int32_t hi = e0 <= q0w ? 0 : (e0 >= q0w + 32 ? 32 : e0 - q0w);
+          if (hi <= lo) return 0u;
+          const uint32_t upto_hi = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
+          return upto_hi & ~((1u << lo) - 1u);  // lo < 32 here
+        };
+        word = bits(a.mask.lts[jk], a.mask.lte[jk]) | bits(a.mask.uts[jk], a.mask.ute[jk]);
+      }
+      mw_lds[buf * 4 * C::BN + w * C::BN + mkey] = word;
+    }
+  };
+
+  f32x16 dq_acc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) dq_acc[db] = f32x16{};
+
+  int entry = cnt > 0 ? __builtin_amdgcn_readfirstlane(lst[0]) : 0;
+
+  auto body = [&](const int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    const int kb = entry >> 1;
+    const bool test = (entry & 1) || (kb == last_kb && ragged);
+    const int next = it + 1 < cnt ? __builtin_amdgcn_readfirstlane(lst[it + 1]) : 0;
+    wait_vmem();      // this wave's loads of tile `it` have landed in LDS
+    __syncthreads();  // ... everyone's, and the mask words
+    if (it + 1 < cnt) issue_tile(next, std::integral_constant<int, buf ^ 1>{});
+
+    const unsigned char* kt = kv_lds + buf * 2 * C::TILE_BYTES;
+    const unsigned char* vt = kt + C::TILE_BYTES;
+
+    // S^T = K Q^T and dP^T = V dO^T: register r of group g in row block rb is tile key
+    // rb*32 + perm_index(r, g); the column is this lane's query.
+    f32x16 sacc[C::NRB], pacc[C::NRB];
+#pragma unroll
+    for (int rb = 0; rb < C::NRB; ++rb) {
+      sacc[rb] = f32x16{};
+      pacc[rb] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < C::QK_STEPS; ++st) {
+        const int off = off_s[st] + rb * 32 * C::ROW_BYTES;
+        const frag ka = *reinterpret_cast<const frag*>(kt + off);
+        const frag va = *reinterpret_cast<const frag*>(vt + off);
+        sacc[rb] = E::mfma(ka, qf[st], sacc[rb]);
+        pacc[rb] = E::mfma(va, dof[st], pacc[rb]);
+      }
+    }
+
+    if (test) {
+      const uint32_t* mw = mw_lds + buf * 4 * C::BN + w * C::BN;
+#pragma unroll
+      for (int rb = 0; rb < C::NRB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t word = mw[rb * 32 + perm_index<KPL>(r, g)];
+          sacc[rb][r] = ((word >> l32) & 1u) ? -INFINITY : sacc[rb][r];
+        }
+    }
+
+    // dS^T = P^T (dP^T - D) as operand fragments: k-step t covers tile keys
+    // t*KSTEP + g*KPL + e = registers (t*KPL)%16 + e of row block (t*KPL)/16.
+    frag sf[C::KV_STEPS];
+#pragma unroll
+    for (int t = 0; t < C::KV_STEPS; ++t) {
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {
+        const int rb = (t * KPL) / 16, r = (t * KPL) % 16 + e;
+        const float p = fast_exp2(fmaf(sacc[rb][r], cexp, -lse2));
+        const float ds = p * (pacc[rb][r] - dlt);
+        if constexpr (KPL == 1)
+          sf[t] = ds;
+        else
+          sf[t][e] = E::from_float(ds);
+      }
+    }
+
+    // dQ^T += K^T dS^T (contraction over the tile's keys; K^T read with the transpose read)
+#pragma unroll
+    for (int t = 0; t < C::KV_STEPS; ++t)
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+        dq_acc[db] = E::mfma(tr_operand(kt, off_tk[db], t * KSTEP * C::ROW_BYTES), sf[t], dq_acc[db]);
+
+    entry = next;
+  };
+
+  if (cnt > 0) issue_tile(entry, std::integral_constant<int, 0>{});
+  // Unrolled by two so each buffer index is a compile-time constant.
+  for (int it = 0; it < cnt; it += 2) {
+    body(it, std::integral_constant<int, 0>{});
+    if (it + 1 < cnt) body(it + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (row_ok) {
+    T* orow = static_cast<T*>(a.dq) + ((size_t)bh * a.nq + q_row) * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * g;
+        const float s = a.scale;
+        if constexpr (sizeof(T) == 2) {
+          uint2 out;
+          out.x = pack_bf16x2(dq_acc[db][4 * i + 0] * s, dq_acc[db][4 * i + 1] * s);
+          out.y = pack_bf16x2(dq_acc[db][4 * i + 2] * s, dq_acc[db][4 * i + 3] * s);
+          *reinterpret_cast<uint2*>(orow + d0) = out;
+        } else {
+          *reinterpret_cast<float4*>(orow + d0) =
+              make_float4(dq_acc[db][4 * i + 0] * s, dq_acc[db][4 * i + 1] * s,
+                          dq_acc[db][4 * i + 2] * s, dq_acc[db][4 * i + 3] * s);
+        }
+      }
+  }
+}
+
+template <typename T, int D>
+hipError_t run_dq(const DqArgs& a, hipStream_t stream, hipEvent_t ev_end) {
+  using C = DqTile<T, D>;
+  const size_t smem = 4 * C::TILE_BYTES + 2 * C::MW_BYTES;
+  // More than 64 KiB of LDS; allow it on the current device.
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_dq_kernel<T, D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (err != hipSuccess) return err;
+  const int64_t n_qb = (a.nq + C::BM - 1) / C::BM;
+  const int64_t grid = n_qb * a.B * a.H;
+  hipLaunchKernelGGL((attn_dq_kernel<T, D>), dim3((unsigned)grid), dim3(256), smem, stream, a);
+  err = hipGetLastError();
+  if (ev_end) (void)hipEventRecord(ev_end, stream);
+  return err;
+}
+
+}  // namespace
+
+hipError_t launch_attn_dq(int dtype, const DqArgs& a, hipStream_t stream, hipEvent_t ev_end) {
+  // The lists were built at the forward's tile shape; this kernel walks them at the same shape.
+  const TileShape t = tile_shape(dtype);
+  if (t.bm_fwd != DqTile<bf16, 128>::BM || t.bn_fwd != DqTile<bf16, 128>::BN) return hipErrorInvalidValue;
+  return dtype == 0 ? run_dq<bf16, 128>(a, stream, ev_end) : run_dq<float, 64>(a, stream, ev_end);
+}
+
+}  // namespace fm

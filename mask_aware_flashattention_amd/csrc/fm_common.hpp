@@ -96,6 +96,30 @@ __host__ __device__ inline uint32_t stretch_len(int32_t s, int32_t e) {
   return e > s ? (uint32_t)e - (uint32_t)s : 0u;
 }
 
+// ---- swizzled LDS tiles ------------------------------------------------------------------------
+// XOR swizzles of 16-byte chunks (bf16 only; fp32 tiles are left plain).  For 256-byte rows
+// (Q, dO, K tiles): chunk c of row r sits at c ^ swz_row(r), a bijection on 16 consecutive rows
+// (conflict-free row reads of 16 rows at one chunk) whose bits 2..3 differ across 4 consecutive
+// rows (conflict-free transpose reads: 4 rows x 4 chunks per 32 lanes).  For the 128-byte dS^T
+// rows the same two properties hold with swz_ds over 8 chunks and the 64-bank pairs of rows.
+template <typename T>
+__device__ __host__ constexpr int swz_row(int r) {
+  return sizeof(T) == 2 ? (((r & 3) << 2) | ((r >> 2) & 3)) : 0;
+}
+template <typename T>
+__device__ __host__ constexpr int swz_ds(int k) {
+  return sizeof(T) == 2 ? ((((k >> 1) & 1) << 2) | ((k >> 2) & 3)) : 0;
+}
+
+// Byte offset of element (row, col) in a tile of `row_bytes`-byte rows with swizzle kind SK
+// (0 = swz_row, 1 = swz_ds).
+template <typename T, int SK>
+__device__ inline int tile_off(int row, int col, int row_bytes) {
+  constexpr int CH = 16 / (int)sizeof(T);
+  const int sw = SK == 0 ? swz_row<T>(row) : swz_ds<T>(row);
+  return row * row_bytes + (((col / CH) ^ sw) * 16) + (col % CH) * (int)sizeof(T);
+}
+
 // ---- XCD-aware work order ---------------------------------------------------------------------
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i to XCD i % 8), each with
 // its own L2.  This maps the dispatch index to a work index so that every XCD walks one

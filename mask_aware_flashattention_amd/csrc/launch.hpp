@@ -53,6 +53,7 @@ struct FwdArgs {
 hipError_t launch_attn_fwd(int dtype, const FwdArgs& a, hipStream_t stream, hipEvent_t ev_begin,
                            hipEvent_t ev_end);
 
+// Backward, key-stationary part: D = rowsum(dO * O) and LSE * log2(e) (bwd_pre), then dK, dV.
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -61,20 +62,38 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   MaskVecs mask;
-  void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;  // float32 [B,H,nq,d]
   float* delta;   // float32 [B,H,nq]
   float* lse2;    // float32 [B,H,nq]: LSE * log2(e), +inf on fully masked rows
   const int32_t* kcnt;
   const int32_t* klist;
-  int32_t list_stride;  // n_qb
+  int32_t list_stride;  // n_qb at the backward tile shape
   int32_t B, H, nq, nk;
   float scale;
 };
-hipError_t launch_attn_bwd(int dtype, const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin,
-                           hipEvent_t ev_end);
+// Runs bwd_pre and the dK/dV kernel; ev_begin (may be null) is recorded before the dK/dV kernel.
+hipError_t launch_attn_bwd(int dtype, const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin);
+
+// Backward, query-stationary part: dQ over the forward's tile lists (needs delta and lse2 from
+// launch_attn_bwd on the same stream).
+struct DqArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  MaskVecs mask;
+  void* dq;
+  const float* delta;
+  const float* lse2;
+  const int32_t* qcnt;
+  const int32_t* qlist;
+  int32_t list_stride;  // n_kb at the forward tile shape
+  int32_t B, H, nq, nk;
+  float scale;
+};
+// ev_end (may be null) is recorded after the dQ kernel.
+hipError_t launch_attn_dq(int dtype, const DqArgs& a, hipStream_t stream, hipEvent_t ev_end);
 
 // Tile shapes of the attention kernels (the shapes tiles are classified at).
 struct TileShape {

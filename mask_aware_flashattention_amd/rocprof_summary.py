@@ -4,8 +4,10 @@
       per-kernel call counts and average / total durations (microseconds), as markdown.
 
   python -m mask_aware_flashattention_amd.rocprof_summary traffic --fetch DB --write DB
-         --kernel SUBSTR --copy-mib N [--command C]
-      HBM bytes per launch of one kernel from a FETCH_SIZE run and a WRITE_SIZE run, each scaled
+         --kernel SUBSTR [SUBSTR ...] --copy-mib N [--command C]
+      HBM bytes per launch of one kernel (or the sum over several kernels that together make
+      one call, e.g. the backward's dK/dV and dQ kernels) from a FETCH_SIZE run and a
+      WRITE_SIZE run, each scaled
       by what the same counter reads for the plain device copy of N MiB that the benchmark runs
       with --calibration-copy-mib N (known bytes / counter bytes).  Prints one JSON object that
       also records the hash of the kernel sources, so the benchmark can tell when the counters
@@ -70,9 +72,10 @@ def cmd_traffic(a):
     f_copy, w_copy = _pick(fetch, COPY_KERNEL), _pick(write, COPY_KERNEL)
     f_factor = copy_bytes / (f_copy * 1024.0)
     w_factor = copy_bytes / (w_copy * 1024.0)
-    f_k, w_k = _pick(fetch, a.kernel), _pick(write, a.kernel)
+    f_k = sum(_pick(fetch, k) for k in a.kernel)
+    w_k = sum(_pick(write, k) for k in a.kernel)
     rec = {
-        "kernel": a.kernel,
+        "kernel": " + ".join(a.kernel),
         "fetch_kib_per_launch": f_k,
         "write_kib_per_launch": w_k,
         "copy_mib": a.copy_mib,
@@ -97,7 +100,7 @@ def main():
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", required=True, nargs="+")
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--sources", default="bwd", choices=["bwd", "fwd"])
     t.add_argument("--command", default="")

@@ -73,9 +73,11 @@ def test_workspace_sizes(lib):
     n_qb, n_kb = 3, 4      # forward tiles 128 x 64
     r = lambda x: -(-x // 256) * 256
     assert lib.flashmask_fwd_workspace_bytes(ctypes.byref(s)) == r(32 * n_kb) + r(4 * n_qb) + r(4 * n_qb * n_kb)
-    n_qb, n_kb = 5, 2      # backward tiles 64 x 128
+    n_qb, n_kb = 5, 2      # dK/dV lists at tiles 64 x 128
+    f_qb, f_kb = 3, 4      # dQ lists at the forward tiles 128 x 64
     rows = 1 * 2 * 300
-    want = r(32 * n_kb) + r(4 * n_kb) + r(4 * n_qb * n_kb) + 2 * r(4 * rows) + r(4 * rows * 128)
+    want = (r(32 * n_kb) + r(4 * n_kb) + r(4 * n_qb * n_kb)
+            + r(32 * f_kb) + r(4 * f_qb) + r(4 * f_qb * f_kb) + 2 * r(4 * rows))
     assert lib.flashmask_bwd_workspace_bytes(ctypes.byref(s)) == want
     assert lib.flashmask_fwd_workspace_bytes(ctypes.byref(shape(d=64))) == 0
     assert lib.flashmask_classify_workspace_bytes(1000, 64) == 512
