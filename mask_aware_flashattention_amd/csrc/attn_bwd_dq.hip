@@ -236,11 +236,14 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   };
 
   if (cnt > 0) issue_tile(entry, std::integral_constant<int, 0>{});
-  // Unrolled by two so each buffer index is a compile-time constant.
-  for (int it = 0; it < cnt; it += 2) {
+  // Unrolled by two so each buffer index is a compile-time constant; an odd last tile runs after
+  // the loop, so the loop body has no conditional path the accumulators must merge across.
+  int it = 0;
+  for (; it + 1 < cnt; it += 2) {
     body(it, std::integral_constant<int, 0>{});
-    if (it + 1 < cnt) body(it + 1, std::integral_constant<int, 1>{});
+    body(it + 1, std::integral_constant<int, 1>{});
   }
+  if (it < cnt) body(it, std::integral_constant<int, 0>{});
 
   if (row_ok) {
     T* orow = static_cast<T*>(a.dq) + ((size_t)bh * a.nq + q_row) * D;
