@@ -36,10 +36,8 @@ struct BwdTile {
   static constexpr int CH = 16 / (int)sizeof(T);
   static constexpr int CPR = D / CH;               // 16-byte chunks per Q / dO / K row
   static constexpr int ROW_BYTES = D * (int)sizeof(T);
-  static constexpr int NQB = BM / 32;
   static constexpr int NDB = D / 32;
   static constexpr int QK_STEPS = D / KSTEP;
-  static constexpr int PQ_STEPS = BM / KSTEP;  // k-steps over a tile's queries
   static constexpr int TILE_BYTES = BM * ROW_BYTES;
   static_assert(CPR == 16, "tile loads assume 256-byte rows");
   static_assert(BM * ROW_BYTES == 16 * 1024, "16 blocks of 1 KiB per tile");
@@ -56,10 +54,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   using frag = typename E::frag;
   constexpr int KPL = C::KPL, KSTEP = C::KSTEP;
 
-  // LDS: two (Q, dO) tile buffers and two (LSE, D) rows.
+  // LDS: three tile buffers [Q | dO | LSE2 | D].
+  constexpr int BUF_BYTES = 2 * C::TILE_BYTES + 2 * C::BM * (int)sizeof(float);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* qdo_lds = smem;                                         // [2][Q | dO]
-  float* rows_lds = reinterpret_cast<float*>(smem + 4 * C::TILE_BYTES);  // [2][LSE2 | D]
+  auto bufp = [&](int b) -> unsigned char* { return smem + b * BUF_BYTES; };
+  auto rowsp = [&](int b) -> float* { return reinterpret_cast<float*>(smem + b * BUF_BYTES + 2 * C::TILE_BYTES); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -100,6 +99,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   }
   MaskRegs mk = {0, 0, 0, 0};  // this lane's key; past the last key every row is masked
   if (key_ok) mk = {a.mask.lts[key], a.mask.lte[key], a.mask.uts[key], a.mask.ute[key]};
+  // Wait for these loads here: the main loop keeps tile loads in flight, and a wait the compiler
+  // would place there for a register loaded now would also wait for those.
+  wait_vmem();
   const bool ragged_block = (kb == n_kb - 1) && (a.nk % C::BN) != 0;
 
   // ---- per-lane LDS byte offsets, constant for the whole kernel ------------------------------
@@ -151,28 +153,36 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   const int32_t* __restrict__ lst = a.klist + (size_t)kb * a.list_stride;
   const float cexp = a.scale * kLog2e;
 
-  // Stage tile `entry` into buffer `buf` with loads straight into LDS: the tile's 64 rows of Q
-  // (then dO) are 16 blocks of 1 KiB; wave w fills blocks 4w..4w+3, lane l the 16-byte slot l
-  // of a block, i.e. row 4j + l/16, physical chunk l%16, which holds logical chunk
-  // (l%16) ^ swz_row(row).  Rows past nq read as zeros.  Waves 0 and 1 also copy the tile's
-  // LSE2 and D rows.
-  auto issue_tile = [&](int entry, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    unsigned char* qt = qdo_lds + buf * 2 * C::TILE_BYTES;
+  // A tile's 64 rows of Q (then dO) are 16 blocks of 1 KiB; wave w moves blocks 4w..4w+3, lane l
+  // the 16-byte slot l of a block, i.e. row 4j + l/16, physical chunk l%16, which holds logical
+  // chunk (l%16) ^ swz_row(row).  Rows past nq read as zeros.  Waves 0 and 1 also move the tile's
+  // LSE2 and D rows.  The loads go to registers first (load_tile) and are written to LDS one
+  // tile later (commit_tile), so no LDS read ever waits on a load in flight.
+  uint4 stq[4], std_[4];
+  float strow = 0.0f;
+  auto load_tile = [&](int entry) {
     const uint32_t tile_base = (uint32_t)(entry >> 1) * C::BM * C::ROW_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = 4 * w + i;
-      const int row = 4 * j + (lane >> 4);
+      const int row = 4 * (4 * w + i) + (lane >> 4);
       const uint32_t voff = (uint32_t)row * C::ROW_BYTES + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
-      buf_load_lds<16>(qbuf, qt + j * 1024, voff, tile_base);
-      buf_load_lds<16>(dobuf, qt + C::TILE_BYTES + j * 1024, voff, tile_base);
+      stq[i] = buf_load16(qbuf, voff, tile_base);
+      std_[i] = buf_load16(dobuf, voff, tile_base);
     }
     if (w < 2) {
       const uint32_t roff = (uint32_t)(entry >> 1) * C::BM * sizeof(float);
-      buf_load_lds<4>(w == 0 ? lbuf : dlbuf, rows_lds + buf * 2 * C::BM + w * C::BM,
-                      (uint32_t)lane * sizeof(float), roff);
+      strow = __builtin_bit_cast(float, buf_load4(w == 0 ? lbuf : dlbuf, (uint32_t)lane * sizeof(float), roff));
     }
+  };
+  auto commit_tile = [&](int b) {
+    unsigned char* qt = bufp(b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * w + i;
+      *reinterpret_cast<uint4*>(qt + j * 1024 + lane * 16) = stq[i];
+      *reinterpret_cast<uint4*>(qt + C::TILE_BYTES + j * 1024 + lane * 16) = std_[i];
+    }
+    if (w < 2) rowsp(b)[w * C::BM + lane] = strow;
   };
 
   // Row mask of this lane's key over a tile's BM query rows starting at q0 (bit i = row q0 + i
@@ -190,146 +200,211 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
     return m >> (g * KPL);
   };
 
-  // List entries are read into scalar registers: the buffer loads take the tile offset as a
-  // scalar operand.
-  int entry = cnt > 0 ? __builtin_amdgcn_readfirstlane(lst[0]) : 0;
-
-  auto body = [&](const int it, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    const int qb = entry >> 1;
-    const bool test = (entry & 1) || ragged_block;
-    const int next = it + 1 < cnt ? __builtin_amdgcn_readfirstlane(lst[it + 1]) : 0;
-    wait_vmem();      // this wave's loads of tile `it` have landed in LDS
-    __syncthreads();  // ... everyone's; buffer buf ^ 1 is free again
-    if (it + 1 < cnt) issue_tile(next, std::integral_constant<int, buf ^ 1>{});
-
-    const unsigned char* qt = qdo_lds + buf * 2 * C::TILE_BYTES;
-    const unsigned char* dt = qt + C::TILE_BYTES;
-    const float* lse_t = rows_lds + buf * 2 * C::BM;
-    const float* dlt_t = lse_t + C::BM;
-    const uint64_t mrow = test ? tile_row_mask(qb * C::BM) : 0ull;
-
-    // The tile is processed as NQB row blocks of 32 queries, one after the other, so only one
-    // block's S, dP, P and dS are live at a time.
+  // ---- one 32-query half ("unit") of a tile, in three steps ---------------------------------
+  // S = Q K^T and dP = dO V^T for the tile's rows h*32..h*32+31: register r of group g is query
+  // h*32 + perm_index(r, g); the column is this lane's key.
+  auto sdp = [&](const unsigned char* qt, auto hc, f32x16& sacc, f32x16& pacc) {
+    constexpr int h = decltype(hc)::value;
+    sacc = f32x16{};
+    pacc = f32x16{};
 #pragma unroll
-    for (int qr = 0; qr < C::NQB; ++qr) {
-      // S = Q K^T and dP = dO V^T for rows qr*32..: register r of group g is tile query
-      // qr*32 + perm_index(r, g); the column is this lane's key.
-      f32x16 sacc = {}, pacc = {};
-      if constexpr (KPL == 8) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int st = 0; st < C::QK_STEPS; ++st) {
-        const int off = off_s[st] + qr * 32 * C::ROW_BYTES;
-        const frag qa = *reinterpret_cast<const frag*>(qt + off);
-        const frag da = *reinterpret_cast<const frag*>(dt + off);
-        sacc = E::mfma(qa, kf[st], sacc);
-        pacc = E::mfma(da, vf[st], pacc);
-      }
-      if constexpr (KPL == 8) {
-        // operand reads one k-step ahead of their MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-#pragma unroll
-        for (int st = 0; st < C::QK_STEPS; ++st) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
-          if (st + 1 < C::QK_STEPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      // LSE (log2 units) and D of the 16 queries this lane holds: runs of KPL consecutive rows
-      // qr*32 + (r/KPL)*2*KPL + g*KPL + 0..KPL-1.
-      float lsev[16], dltv[16];
-      if constexpr (KPL == 8) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int q = qr * 32 + 16 * j + 8 * g;
-          const float4 l0 = *reinterpret_cast<const float4*>(lse_t + q);
-          const float4 l1 = *reinterpret_cast<const float4*>(lse_t + q + 4);
-          const float4 d0 = *reinterpret_cast<const float4*>(dlt_t + q);
-          const float4 d1 = *reinterpret_cast<const float4*>(dlt_t + q + 4);
-          const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-          const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            lsev[8 * j + e] = lv[e];
-            dltv[8 * j + e] = dv[e];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          lsev[r] = lse_t[qr * 32 + perm_index<KPL>(r, g)];
-          dltv[r] = dlt_t[qr * 32 + perm_index<KPL>(r, g)];
-        }
-      }
-
-      // P and dS (overwriting sacc and pacc); the masked variant is a separate code path so
-      // unmasked tiles pay nothing for the test.
-      auto elementwise = [&](auto masked_c) {
-        constexpr bool MASKED = decltype(masked_c)::value;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(sacc[r], cexp, -lsev[r]));
-          if constexpr (MASKED) {
-            const int bit = qr * 32 + perm_index<KPL>(r, 0);
-            p = ((mrow >> bit) & 1ull) ? 0.0f : p;
-          }
-          sacc[r] = p;
-          pacc[r] = p * (pacc[r] - dltv[r]);
-        }
-      };
-      if (test)
-        elementwise(std::true_type{});
-      else
-        elementwise(std::false_type{});
-
-      // Operand fragments of P and dS: k-step u covers tile queries
-      // qr*32 + u*KSTEP + g*KPL + e = registers u*KPL + e.
-#pragma unroll
-      for (int u = 0; u < US; ++u) {
-        frag pf, sf;
-        if constexpr (KPL == 1) {
-          pf = sacc[u];
-          sf = pacc[u];
-        } else {
-#pragma unroll
-          for (int e = 0; e < KPL; ++e) {
-            pf[e] = E::from_float(sacc[u * KPL + e]);
-            sf[e] = E::from_float(pacc[u * KPL + e]);
-          }
-        }
-        const int q0 = qr * 32 + u * KSTEP;
-        // dV^T += dO^T P and dK^T += Q^T dS: A = rows d of the transposed tiles (contraction
-        // over the tile's queries q0..q0+KSTEP), read with the transpose read.
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          dv_acc[db] = E::mfma(tr_operand(dt, off_tq[db], q0 * C::ROW_BYTES), pf, dv_acc[db]);
-          dk_acc[db] = E::mfma(tr_operand(qt, off_tq[db], q0 * C::ROW_BYTES), sf, dk_acc[db]);
-        }
-      }
-      if constexpr (KPL == 8) {
-        // transpose reads (4 per d block) one d block ahead of their two MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
-#pragma unroll
-        for (int i = 0; i < US * C::NDB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);
-          if (i + 1 < US * C::NDB) __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
-        }
-      }
+    for (int st = 0; st < C::QK_STEPS; ++st) {
+      const int off = off_s[st] + h * 32 * C::ROW_BYTES;
+      const frag qa = *reinterpret_cast<const frag*>(qt + off);
+      const frag da = *reinterpret_cast<const frag*>(qt + C::TILE_BYTES + off);
+      sacc = E::mfma(qa, kf[st], sacc);
+      pacc = E::mfma(da, vf[st], pacc);
     }
-
-    entry = next;
   };
 
-  if (cnt > 0) issue_tile(entry, std::integral_constant<int, 0>{});
-  // Unrolled by two so each buffer index is a compile-time constant; an odd last tile runs after
-  // the loop, so the loop body has no conditional path the accumulators must merge across.
-  int it = 0;
-  for (; it + 1 < cnt; it += 2) {
-    body(it, std::integral_constant<int, 0>{});
-    body(it + 1, std::integral_constant<int, 1>{});
+  // P = exp2(S*scale*log2e - LSE2) (0 where masked: bit h*32 + perm_index(r, 0) of mrow) and
+  // dS = P (dP - D), rounded into operand fragments: k-step u covers queries
+  // h*32 + u*KSTEP + g*KPL + e = registers u*KPL + e.
+  struct Rows {
+    float lse[16], dlt[16];  // LSE2 and D of the 16 queries this lane holds
+  };
+  auto load_rows = [&](const float* lse_t, auto hc, Rows& rw) {
+    constexpr int h = decltype(hc)::value;
+    const float* dlt_t = lse_t + C::BM;
+    if constexpr (KPL == 8) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int q = h * 32 + 16 * j + 8 * g;
+        const float4 l0 = *reinterpret_cast<const float4*>(lse_t + q);
+        const float4 l1 = *reinterpret_cast<const float4*>(lse_t + q + 4);
+        const float4 d0 = *reinterpret_cast<const float4*>(dlt_t + q);
+        const float4 d1 = *reinterpret_cast<const float4*>(dlt_t + q + 4);
+        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          rw.lse[8 * j + e] = lv[e];
+          rw.dlt[8 * j + e] = dv[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        rw.lse[r] = lse_t[h * 32 + perm_index<KPL>(r, g)];
+        rw.dlt[r] = dlt_t[h * 32 + perm_index<KPL>(r, g)];
+      }
+    }
+  };
+  // One 32-query unit with a fixed issue order (a wave per SIMD issues in order): the next
+  // unit's S / dP products are interleaved with this unit's elementwise work
+  //   P = exp2(S*scale*log2e - LSE2) (0 where masked), dS = P (dP - D),
+  // then dV^T += dO^T P and dK^T += Q^T dS run with their transpose reads.  sched_barrier fences
+  // pin the order; operand reads run a few products ahead of their use.
+  auto unit = [&](const unsigned char* qt, auto hc, auto maskedc, uint64_t mrow, const Rows& rw,
+                  const f32x16& sc, const f32x16& pc, const unsigned char* qn, auto hnc,
+                  auto nextc, const float* lse_n, Rows& rw_n, f32x16& sn, f32x16& pn) {
+    constexpr int h = decltype(hc)::value, hn = decltype(hnc)::value;
+    constexpr bool MASKED = decltype(maskedc)::value;
+    constexpr bool NEXT = decltype(nextc)::value;
+    constexpr int NS = 2 * C::QK_STEPS, AH = 4;  // S / dP products of a unit, read-ahead
+    constexpr int NDV = 2 * US * C::NDB, AT = 3;  // dV / dK products of a unit, read-ahead
+    // Registers 0..7 feed the first half of the dV / dK products, 8..15 the second half: the
+    // elementwise work of registers 0..RA-1 runs beside the S / dP products, the rest beside the
+    // first half of the dV / dK products.
+    constexpr int RA = 10;
+    if constexpr (NEXT) load_rows(lse_n, hnc, rw_n);
+    auto sread = [&](int i) -> frag {
+      return *reinterpret_cast<const frag*>(qn + ((i & 1) ? C::TILE_BYTES : 0) + off_s[i >> 1] +
+                                            hn * 32 * C::ROW_BYTES);
+    };
+    // dV / dK product j: k-step u = j / (2 NDB), d block (j % (2 NDB)) / 2, dV (even j) or dK
+    auto tread = [&](int j) -> frag {
+      const int u = j / (2 * C::NDB), db = (j % (2 * C::NDB)) >> 1;
+      return tr_operand((j & 1) ? qt : qt + C::TILE_BYTES, off_tq[db], (h * 32 + u * KSTEP) * C::ROW_BYTES);
+    };
+    frag op[NS], top[NDV];
+    if constexpr (NEXT) {
+      sn = f32x16{};
+      pn = f32x16{};
+#pragma unroll
+      for (int i = 0; i < AH; ++i) op[i] = sread(i);
+    }
+    // P = exp2(S*scale*log2e - LSE2) and dS = P (dP - D) for register r.  Masked entries get an
+    // exponent of -inf: sbfe gives 0 or all ones (bit perm_index(r, 0) of this unit's word), and
+    // the bitfield insert picks -inf's bit pattern.
+    const uint32_t mw = (uint32_t)(mrow >> (32 * h));
+    float pv[16], dsv[16];
+    auto elem = [&](int r) {
+      uint32_t x = __float_as_uint(fmaf(sc[r], cexp, -rw.lse[r]));
+      if constexpr (MASKED) {
+        const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)mw, perm_index<KPL>(r, 0), 1);
+        x = (x & ~m) | (m & 0xff800000u);
+      }
+      pv[r] = fast_exp2(__uint_as_float(x));
+      dsv[r] = pv[r] * (pc[r] - rw.dlt[r]);
+    };
+    // operand fragments: k-step u covers queries h*32 + u*KSTEP + g*KPL + e = registers u*KPL + e
+    frag pf[US], sf[US];
+    auto frags = [&](int u) {
+      if constexpr (KPL == 1) {
+        pf[u] = pv[u];
+        sf[u] = dsv[u];
+      } else {
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          pf[u][e] = E::from_float(pv[u * KPL + e]);
+          sf[u][e] = E::from_float(dsv[u * KPL + e]);
+        }
+      }
+    };
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if constexpr (NEXT) {
+        if (i & 1)
+          pn = E::mfma(op[i], vf[i >> 1], pn);
+        else
+          sn = E::mfma(op[i], kf[i >> 1], sn);
+        if (i + AH < NS) op[i + AH] = sread(i + AH);
+      }
+#pragma unroll
+      for (int r = i * RA / NS; r < (i + 1) * RA / NS; ++r) elem(r);
+      if (i + AT >= NS) top[i + AT - NS] = tread(i + AT - NS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < US / 2; ++u) frags(u);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int HALF = NDV / 2;
+#pragma unroll
+    for (int j = 0; j < NDV; ++j) {
+      const int u = j / (2 * C::NDB), db = (j % (2 * C::NDB)) >> 1;
+      if (j & 1)
+        dk_acc[db] = E::mfma(top[j], sf[u], dk_acc[db]);
+      else
+        dv_acc[db] = E::mfma(top[j], pf[u], dv_acc[db]);
+      if (j + AT < NDV) top[j + AT] = tread(j + AT);
+      if (j < HALF) {
+#pragma unroll
+        for (int r = RA + j * (16 - RA) / HALF; r < RA + (j + 1) * (16 - RA) / HALF; ++r) elem(r);
+        if (j == HALF - 1) {
+#pragma unroll
+          for (int u = US / 2; u < US; ++u) frags(u);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- software pipeline over units -----------------------------------------------------------
+  // Tile t sits in buffer t % 3.  While the elementwise step of one unit runs, the S / dP
+  // products of the next unit (the second half of the tile, or the first half of the next tile)
+  // are already issued.  Tile t+1 is waited for, with one workgroup barrier, before the second
+  // unit of tile t; that barrier also frees the buffer of tile t-1, which then receives tile t+2.
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
+  f32x16 sn, pn;  // S / dP of the next unit
+  Rows rw, rw_n;  // LSE2 / D of the current and the next unit
+  int entry = 0, cur = 0;
+  if (cnt > 0) {
+    entry = __builtin_amdgcn_readfirstlane(lst[0]);
+    load_tile(entry);
+    wait_vmem();
+    commit_tile(0);
+    __syncthreads();
+    if (cnt > 1) load_tile(__builtin_amdgcn_readfirstlane(lst[1]));
+    load_rows(rowsp(0), H0{}, rw);
+    sdp(bufp(0), H0{}, sn, pn);
   }
-  if (it < cnt) body(it, std::integral_constant<int, 0>{});
+  // Tile t sits in buffer t % 3.
+  auto tile_step = [&](const int t, auto has_next_c, auto maskedc) {
+    constexpr bool HAS_NEXT = decltype(has_next_c)::value;
+    const bool test = (entry & 1) || ragged_block;
+    const uint64_t mrow = decltype(maskedc)::value && test ? tile_row_mask((entry >> 1) * C::BM) : 0ull;
+    const unsigned char* qt = bufp(cur);
+    const float* lse_t = rowsp(cur);
+    const int nxt = cur == 2 ? 0 : cur + 1;
+    // first half, with the second half's S / dP
+    f32x16 sc = sn, pc = pn;
+    unit(qt, H0{}, maskedc, mrow, rw, sc, pc, qt, H1{}, std::true_type{}, lse_t, rw_n, sn, pn);
+    rw = rw_n;
+    sc = sn;
+    pc = pn;
+    if constexpr (HAS_NEXT) {
+      // second half, with the next tile's first half
+      entry = __builtin_amdgcn_readfirstlane(lst[t + 1]);
+      wait_vmem();        // tile t+1 is in this wave's registers
+      commit_tile(nxt);   // its buffer last held tile t-2
+      __syncthreads();    // tile t+1 complete in LDS
+      if (t + 2 < cnt) load_tile(__builtin_amdgcn_readfirstlane(lst[t + 2]));
+      unit(qt, H1{}, maskedc, mrow, rw, sc, pc, bufp(nxt), H0{}, std::true_type{}, rowsp(nxt),
+           rw_n, sn, pn);
+      rw = rw_n;
+    } else {
+      unit(qt, H1{}, maskedc, mrow, rw, sc, pc, qt, H0{}, std::false_type{}, lse_t, rw_n, sn, pn);
+    }
+    cur = nxt;
+  };
+  // Every tile takes the row test (an unmasked tile's mask word is zero): one code path keeps
+  // the loop free of branches the accumulators would have to merge across.
+  auto step = [&](const int t, auto has_next_c) { tile_step(t, has_next_c, std::true_type{}); };
+  for (int t = 0; t + 1 < cnt; ++t) step(t, std::true_type{});
+  if (cnt > 0) step(cnt - 1, std::false_type{});
 
   if (key_ok) {
     T* dkr = static_cast<T*>(a.dk) + ((size_t)bh * a.nk + key) * D;
@@ -390,12 +465,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
 }
 
 template <typename T, int D>
-size_t bwd_smem_bytes() {
-  using C = BwdTile<T, D>;
-  return 4 * C::TILE_BYTES + sizeof(float) * 4 * C::BM;
-}
-
-template <typename T, int D>
 hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin) {
   const int64_t rows = (int64_t)a.B * a.H * a.nq;
   const int pre_grid = (int)((rows + 15) / 16);
@@ -405,12 +474,13 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
-  const size_t smem = bwd_smem_bytes<T, D>();
+  using C = BwdTile<T, D>;
+  const size_t smem = 3 * (2 * C::TILE_BYTES + 2 * C::BM * sizeof(float));
   // The main kernel uses more than 64 KiB of LDS; allow it on the current device.
   err = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_kernel<T, D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
-  const int64_t n_kb = (a.nk + BwdTile<T, D>::BN - 1) / BwdTile<T, D>::BN;
+  const int64_t n_kb = (a.nk + C::BN - 1) / C::BN;
   const int64_t grid = n_kb * a.B * a.H;
   if (ev_begin) (void)hipEventRecord(ev_begin, stream);
   hipLaunchKernelGGL((attn_bwd_kernel<T, D>), dim3((unsigned)grid), dim3(256), smem, stream, a);
