@@ -255,13 +255,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   //   P = exp2(S*scale*log2e - LSE2) (0 where masked), dS = P (dP - D),
   // then dV^T += dO^T P and dK^T += Q^T dS run with their transpose reads.  sched_barrier fences
   // pin the order; operand reads run a few products ahead of their use.
-  auto unit = [&](const unsigned char* qt, auto hc, auto maskedc, uint64_t mrow, const Rows& rw,
-                  const f32x16& sc, const f32x16& pc, const unsigned char* qn, auto hnc,
-                  auto nextc, const float* lse_n, Rows& rw_n, f32x16& sn, f32x16& pn) {
-    constexpr int h = decltype(hc)::value, hn = decltype(hnc)::value;
+  constexpr int AH = 4;  // operand reads of the S / dP products issued ahead of their use
+  // The first AH operand reads of a unit's S / dP products can be issued by the unit before it
+  // (pre: they are already in opio; pfn: issue the following unit's into opio, from tile q2,
+  // half h2, at the end of this unit).
+  auto unit = [&](const unsigned char* qt, auto hc, auto maskedc, bool test, uint64_t mrow,
+                  const Rows& rw, const f32x16& sc, const f32x16& pc, const unsigned char* qn,
+                  auto hnc, auto nextc, const float* lse_n, Rows& rw_n, f32x16& sn, f32x16& pn,
+                  frag* opio, auto prec, auto pfnc, const unsigned char* q2, auto h2c,
+                  auto barc, auto&& bar) {
+    constexpr int h = decltype(hc)::value, hn = decltype(hnc)::value, h2 = decltype(h2c)::value;
     constexpr bool MASKED = decltype(maskedc)::value;
     constexpr bool NEXT = decltype(nextc)::value;
-    constexpr int NS = 2 * C::QK_STEPS, AH = 4;  // S / dP products of a unit, read-ahead
+    constexpr bool PRE = decltype(prec)::value, PFN = decltype(pfnc)::value;
+    constexpr bool BAR = decltype(barc)::value;  // run bar() before the read-ahead at the end
+    constexpr int NS = 2 * C::QK_STEPS;  // S / dP products of a unit
     constexpr int NDV = 2 * US * C::NDB, AT = 3;  // dV / dK products of a unit, read-ahead
     // Registers 0..7 feed the first half of the dV / dK products, 8..15 the second half: the
     // elementwise work of registers 0..RA-1 runs beside the S / dP products, the rest beside the
@@ -282,21 +290,28 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
       sn = f32x16{};
       pn = f32x16{};
 #pragma unroll
-      for (int i = 0; i < AH; ++i) op[i] = sread(i);
+      for (int i = 0; i < AH; ++i) op[i] = PRE ? opio[i] : sread(i);
     }
-    // P = exp2(S*scale*log2e - LSE2) and dS = P (dP - D) for register r.  Masked entries get an
-    // exponent of -inf: sbfe gives 0 or all ones (bit perm_index(r, 0) of this unit's word), and
-    // the bitfield insert picks -inf's bit pattern.
-    const uint32_t mw = (uint32_t)(mrow >> (32 * h));
+    // P = exp2(S*scale*log2e - LSE2) and dS = P (dP - D) for register r.
     float pv[16], dsv[16];
     auto elem = [&](int r) {
-      uint32_t x = __float_as_uint(fmaf(sc[r], cexp, -rw.lse[r]));
-      if constexpr (MASKED) {
-        const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)mw, perm_index<KPL>(r, 0), 1);
-        x = (x & ~m) | (m & 0xff800000u);
-      }
-      pv[r] = fast_exp2(__uint_as_float(x));
+      pv[r] = fast_exp2(fmaf(sc[r], cexp, -rw.lse[r]));
       dsv[r] = pv[r] * (pc[r] - rw.dlt[r]);
+    };
+    // In partly masked tiles P and dS are zeroed where masked (bit perm_index(r, 0) of this
+    // unit's mask word) before they are rounded into operands; other tiles skip this.
+    const uint32_t mw = (uint32_t)(mrow >> (32 * h));
+    auto apply_mask = [&](int r0, int r1) {
+      if constexpr (MASKED) {
+        if (test) {  // uniform across the wave
+#pragma unroll
+          for (int r = r0; r < r1; ++r) {
+            const bool m = (mw >> perm_index<KPL>(r, 0)) & 1u;
+            pv[r] = m ? 0.0f : pv[r];
+            dsv[r] = m ? 0.0f : dsv[r];
+          }
+        }
+      }
     };
     // operand fragments: k-step u covers queries h*32 + u*KSTEP + g*KPL + e = registers u*KPL + e
     frag pf[US], sf[US];
@@ -327,6 +342,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
       if (i + AT >= NS) top[i + AT - NS] = tread(i + AT - NS);
       __builtin_amdgcn_sched_barrier(0);
     }
+    apply_mask(0, 8);
 #pragma unroll
     for (int u = 0; u < US / 2; ++u) frags(u);
     __builtin_amdgcn_sched_barrier(0);
@@ -339,10 +355,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
       else
         dv_acc[db] = E::mfma(top[j], pf[u], dv_acc[db]);
       if (j + AT < NDV) top[j + AT] = tread(j + AT);
+      if constexpr (BAR) {
+        if (j == NDV - AH - 1) bar();
+      }
+      if constexpr (PFN) {
+        if (j >= NDV - AH) {
+          const int i = j - (NDV - AH);
+          opio[i] = *reinterpret_cast<const frag*>(q2 + ((i & 1) ? C::TILE_BYTES : 0) + off_s[i >> 1] +
+                                                   h2 * 32 * C::ROW_BYTES);
+        }
+      }
       if (j < HALF) {
 #pragma unroll
         for (int r = RA + j * (16 - RA) / HALF; r < RA + (j + 1) * (16 - RA) / HALF; ++r) elem(r);
         if (j == HALF - 1) {
+          apply_mask(8, 16);
 #pragma unroll
           for (int u = US / 2; u < US; ++u) frags(u);
         }
@@ -360,6 +387,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   using H1 = std::integral_constant<int, 1>;
   f32x16 sn, pn;  // S / dP of the next unit
   Rows rw, rw_n;  // LSE2 / D of the current and the next unit
+  frag opio[AH];  // operands read ahead for the next unit's S / dP products
   int entry = 0, cur = 0;
   if (cnt > 0) {
     entry = __builtin_amdgcn_readfirstlane(lst[0]);
@@ -370,6 +398,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
     if (cnt > 1) load_tile(__builtin_amdgcn_readfirstlane(lst[1]));
     load_rows(rowsp(0), H0{}, rw);
     sdp(bufp(0), H0{}, sn, pn);
+#pragma unroll
+    for (int i = 0; i < AH; ++i)
+      opio[i] = *reinterpret_cast<const frag*>(bufp(0) + ((i & 1) ? C::TILE_BYTES : 0) + off_s[i >> 1] +
+                                               32 * C::ROW_BYTES);
   }
   // Tile t sits in buffer t % 3.
   auto tile_step = [&](const int t, auto has_next_c, auto maskedc) {
@@ -381,7 +413,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
     const int nxt = cur == 2 ? 0 : cur + 1;
     // first half, with the second half's S / dP
     f32x16 sc = sn, pc = pn;
-    unit(qt, H0{}, maskedc, mrow, rw, sc, pc, qt, H1{}, std::true_type{}, lse_t, rw_n, sn, pn);
+    auto none = [] {};
+    unit(qt, H0{}, maskedc, test, mrow, rw, sc, pc, qt, H1{}, std::true_type{}, lse_t, rw_n, sn, pn,
+         opio, std::true_type{}, std::false_type{}, qt, H0{}, std::false_type{}, none);
     rw = rw_n;
     sc = sn;
     pc = pn;
@@ -392,11 +426,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
       commit_tile(nxt);   // its buffer last held tile t-2
       __syncthreads();    // tile t+1 complete in LDS
       if (t + 2 < cnt) load_tile(__builtin_amdgcn_readfirstlane(lst[t + 2]));
-      unit(qt, H1{}, maskedc, mrow, rw, sc, pc, bufp(nxt), H0{}, std::true_type{}, rowsp(nxt),
-           rw_n, sn, pn);
+      unit(qt, H1{}, maskedc, test, mrow, rw, sc, pc, bufp(nxt), H0{}, std::true_type{},
+           rowsp(nxt), rw_n, sn, pn, opio, std::false_type{}, std::true_type{}, bufp(nxt), H1{},
+           std::false_type{}, none);
       rw = rw_n;
     } else {
-      unit(qt, H1{}, maskedc, mrow, rw, sc, pc, qt, H0{}, std::false_type{}, lse_t, rw_n, sn, pn);
+      unit(qt, H1{}, maskedc, test, mrow, rw, sc, pc, qt, H0{}, std::false_type{}, lse_t, rw_n, sn,
+           pn, opio, std::false_type{}, std::false_type{}, qt, H0{}, std::false_type{}, none);
     }
     cur = nxt;
   };

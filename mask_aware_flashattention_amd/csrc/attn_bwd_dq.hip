@@ -47,10 +47,21 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   using frag = typename E::frag;
   constexpr int KPL = C::KPL, KSTEP = C::KSTEP;
 
-  // LDS: two (K, V) tile buffers, two mask-word buffers.
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* kv_lds = smem;                                   // [2][K | V]
-  uint32_t* mw_lds = reinterpret_cast<uint32_t*>(smem + 4 * C::TILE_BYTES);  // [2][4][BN]
+  // LDS: two buffers [K | V | mask words].  They are separate arrays so that the compiler can
+  // tell that loads into one buffer never overlap reads of the other, and adds no wait on the
+  // loads in flight before those reads.
+  constexpr int BUF_BYTES = 2 * C::TILE_BYTES + C::MW_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[BUF_BYTES];
+  auto bufp = [&](auto bc) -> unsigned char* {
+    if constexpr (decltype(bc)::value == 0)
+      return lds0;
+    else
+      return lds1;
+  };
+  auto mwp = [&](auto bc) -> uint32_t* {
+    return reinterpret_cast<uint32_t*>(bufp(bc) + 2 * C::TILE_BYTES);
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -126,14 +137,13 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
     }
   };
 
-  // Stage key tile `entry` into buffer `buf`: K then V, 16 blocks of 1 KiB each, wave w fills
+  // Stage key tile `entry` into buffer `bufc`: K then V, 16 blocks of 1 KiB each, wave w fills
   // blocks 4w..4w+3 (lane l: row 4j + l/16, physical chunk l%16 = logical chunk
   // (l%16) ^ swz_row(row)); keys past nk read as zeros.  In partly masked tiles thread tid
   // also writes the row mask of key tid%64 for wave tid/64's 32 rows.
   auto issue_tile = [&](int entry, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
     const int kb = entry >> 1;
-    unsigned char* kt = kv_lds + buf * 2 * C::TILE_BYTES;
+    unsigned char* kt = bufp(bufc);
     const uint32_t tile_base = (uint32_t)kb * C::BN * C::ROW_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -158,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
         };
         word = bits(a.mask.lts[jk], a.mask.lte[jk]) | bits(a.mask.uts[jk], a.mask.ute[jk]);
       }
-      mw_lds[buf * 4 * C::BN + w * C::BN + mkey] = word;
+      mwp(bufc)[w * C::BN + mkey] = word;
     }
   };
 
@@ -177,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
     __syncthreads();  // ... everyone's, and the mask words
     if (it + 1 < cnt) issue_tile(next, std::integral_constant<int, buf ^ 1>{});
 
-    const unsigned char* kt = kv_lds + buf * 2 * C::TILE_BYTES;
+    const unsigned char* kt = bufp(bufc);
     const unsigned char* vt = kt + C::TILE_BYTES;
 
     // S^T = K Q^T and dP^T = V dO^T: register r of group g in row block rb is tile key
@@ -198,7 +208,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
     }
 
     if (test) {
-      const uint32_t* mw = mw_lds + buf * 4 * C::BN + w * C::BN;
+      const uint32_t* mw = mwp(bufc) + w * C::BN;
 #pragma unroll
       for (int rb = 0; rb < C::NRB; ++rb)
 #pragma unroll
@@ -270,15 +280,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
 template <typename T, int D>
 hipError_t run_dq(const DqArgs& a, hipStream_t stream, hipEvent_t ev_end) {
   using C = DqTile<T, D>;
-  const size_t smem = 4 * C::TILE_BYTES + 2 * C::MW_BYTES;
-  // More than 64 KiB of LDS; allow it on the current device.
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_dq_kernel<T, D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (err != hipSuccess) return err;
   const int64_t n_qb = (a.nq + C::BM - 1) / C::BM;
   const int64_t grid = n_qb * a.B * a.H;
-  hipLaunchKernelGGL((attn_dq_kernel<T, D>), dim3((unsigned)grid), dim3(256), smem, stream, a);
-  err = hipGetLastError();
+  hipLaunchKernelGGL((attn_dq_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  const hipError_t err = hipGetLastError();
   if (ev_end) (void)hipEventRecord(ev_end, stream);
   return err;
 }
