@@ -153,11 +153,25 @@ int32_t flashmask_classify(const int32_t* LTS, const int32_t* LTE, const int32_t
                            int32_t* klist, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Work order of the attention kernels (a scheduling aid; exposed for testing).  Writes to
+ * order[0..n) a permutation of 0..n-1 in which the block counts cnt[order[k]] >> s never
+ * increase with k, where s is the smallest shift with (n_other >> s) < 2048 (n_other bounds the
+ * counts).  Blocks in one bucket come in no particular order.  The forward and both backward
+ * kernels take their blocks in this order (longest list first), so that the longest-running
+ * workgroups start first; the order changes no result.  "FlashMask-3 ..." (zicq.com summary)
+ * names load balance across ranks as a goal; this is its counterpart inside one GPU.
+ * cnt, order: device int32 [n], 4-byte aligned.  Errors: FM_ERR_NULL, FM_ERR_SHAPE (n < 1 or
+ * n_other < 0), FM_ERR_ALIGN, FM_ERR_HIP.
+ */
+int32_t flashmask_block_order(const int32_t* cnt, int32_t n, int32_t n_other, int32_t* order,
+                              void* stream);
+
+/*
  * Diagnostic hook for timing the attention kernels alone (a benchmark aid; not needed to use the
  * library).  After this call, flashmask_fwd records fwd_begin / fwd_end and flashmask_bwd
  * records bwd_begin / bwd_end (hipEvent_t passed as void*, created by the caller) on the call's
- * stream immediately before and after its attention kernel (the backward's main kernel, without
- * its preprocess and dQ conversion).  NULL disables a pair.  This is the library's only state:
+ * stream immediately before and after its attention kernels (for the backward: before the dK/dV
+ * kernel and after the dQ kernel, without the preprocess).  NULL disables a pair.  This is the library's only state:
  * process-wide, not synchronised; set it from the thread that makes the calls.
  */
 int32_t flashmask_set_profile_events(void* fwd_begin, void* fwd_end, void* bwd_begin,

@@ -58,22 +58,25 @@ int32_t check_scale(float scale) {
 
 fm::TileShape tiles(int32_t dtype) { return fm::tile_shape(dtype); }
 
+// Forward workspace: key-block min/max, query-block lists and the longest-first block order.
 struct FwdWs {
-  size_t mm, qcnt, qlist, total;
+  size_t mm, qcnt, qlist, order, total;
 };
 FwdWs fwd_layout(const Geometry& g) {
   FwdWs w;
   w.mm = 0;
   w.qcnt = w.mm + round_up(sizeof(int32_t) * 8 * g.n_kb);
   w.qlist = w.qcnt + round_up(sizeof(int32_t) * g.n_qb);
-  w.total = w.qlist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb);
+  w.order = w.qlist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb);
+  w.total = w.order + round_up(sizeof(int32_t) * g.n_qb);
   return w;
 }
 
 // Backward workspace: key-block lists at the backward tile shape (dK/dV kernel), query-block
-// lists at the forward tile shape (dQ kernel), and the per-row D and LSE * log2(e).
+// lists at the forward tile shape (dQ kernel), both block orders, and the per-row D and
+// LSE * log2(e).
 struct BwdWs {
-  size_t mm, kcnt, klist, mm_f, qcnt, qlist, delta, lse2, total;
+  size_t mm, kcnt, klist, mm_f, qcnt, qlist, korder, qorder, delta, lse2, total;
 };
 BwdWs bwd_layout(const fm_shape* s, const Geometry& g, const Geometry& gf) {
   BwdWs w;
@@ -84,7 +87,9 @@ BwdWs bwd_layout(const fm_shape* s, const Geometry& g, const Geometry& gf) {
   w.mm_f = w.klist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb);
   w.qcnt = w.mm_f + round_up(sizeof(int32_t) * 8 * gf.n_kb);
   w.qlist = w.qcnt + round_up(sizeof(int32_t) * gf.n_qb);
-  w.delta = w.qlist + round_up(sizeof(int32_t) * gf.n_qb * gf.n_kb);
+  w.korder = w.qlist + round_up(sizeof(int32_t) * gf.n_qb * gf.n_kb);
+  w.qorder = w.korder + round_up(sizeof(int32_t) * g.n_kb);
+  w.delta = w.qorder + round_up(sizeof(int32_t) * gf.n_qb);
   w.lse2 = w.delta + round_up(sizeof(float) * rows);
   w.total = w.lse2 + round_up(sizeof(float) * rows);
   return w;
@@ -160,15 +165,17 @@ int32_t flashmask_fwd(const fm_shape* s, const void* Q, const void* K, const voi
   int32_t* mm = reinterpret_cast<int32_t*>(base + L.mm);
   int32_t* qcnt = reinterpret_cast<int32_t*>(base + L.qcnt);
   int32_t* qlist = reinterpret_cast<int32_t*>(base + L.qlist);
+  int32_t* order = reinterpret_cast<int32_t*>(base + L.order);
   const fm::MaskVecs mv{LTS, LTE, UTS, UTE};
 
   hipError_t e = fm::launch_block_minmax(mv, s->nk, t.bn_fwd, mm, hs);
   if (e == hipSuccess)
     e = fm::launch_classify(mm, (int32_t)g.n_kb, s->nq, t.bm_fwd, nullptr, qcnt, qlist, nullptr,
                             nullptr, hs);
+  if (e == hipSuccess) e = fm::launch_block_order(qcnt, (int32_t)g.n_qb, (int32_t)g.n_kb, order, hs);
   if (e == hipSuccess) {
-    fm::FwdArgs a{Q, K, V, mv, O, LSE, qcnt, qlist, (int32_t)g.n_kb, s->B, s->H, s->nq, s->nk,
-                  scale};
+    fm::FwdArgs a{Q,     K,     V,     mv,   O,    LSE,  qcnt, qlist, order, (int32_t)g.n_kb,
+                  s->B, s->H, s->nq, s->nk, scale};
     e = fm::launch_attn_fwd(s->dtype, a, hs, g_fwd_begin, g_fwd_end);
   }
   return hip_status(e);
@@ -213,6 +220,8 @@ int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const voi
   int32_t* mm_f = reinterpret_cast<int32_t*>(base + L.mm_f);
   int32_t* qcnt = reinterpret_cast<int32_t*>(base + L.qcnt);
   int32_t* qlist = reinterpret_cast<int32_t*>(base + L.qlist);
+  int32_t* korder = reinterpret_cast<int32_t*>(base + L.korder);
+  int32_t* qorder = reinterpret_cast<int32_t*>(base + L.qorder);
   float* delta = reinterpret_cast<float*>(base + L.delta);
   float* lse2 = reinterpret_cast<float*>(base + L.lse2);
   const fm::MaskVecs mv{LTS, LTE, UTS, UTE};
@@ -225,14 +234,16 @@ int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const voi
   if (e == hipSuccess)
     e = fm::launch_classify(mm_f, (int32_t)gf.n_kb, s->nq, t.bm_fwd, nullptr, qcnt, qlist, nullptr,
                             nullptr, hs);
+  if (e == hipSuccess) e = fm::launch_block_order(kcnt, (int32_t)g.n_kb, (int32_t)g.n_qb, korder, hs);
+  if (e == hipSuccess) e = fm::launch_block_order(qcnt, (int32_t)gf.n_qb, (int32_t)gf.n_kb, qorder, hs);
   if (e == hipSuccess) {
-    fm::BwdArgs a{Q,     K,    V,     O,    dO,   LSE,  mv,   dK, dV, delta, lse2, kcnt, klist,
-                  (int32_t)g.n_qb, s->B, s->H, s->nq, s->nk, scale};
+    fm::BwdArgs a{Q,     K,    V,      O,    dO,   LSE,  mv,   dK, dV, delta, lse2, kcnt, klist,
+                  korder, (int32_t)g.n_qb, s->B, s->H, s->nq, s->nk, scale};
     e = fm::launch_attn_bwd(s->dtype, a, hs, g_bwd_begin);
   }
   if (e == hipSuccess) {
     fm::DqArgs a{Q,    K,     V,     dO,    mv,   dQ,   delta, lse2, qcnt, qlist,
-                 (int32_t)gf.n_kb, s->B, s->H, s->nq, s->nk, scale};
+                 qorder, (int32_t)gf.n_kb, s->B, s->H, s->nq, s->nk, scale};
     e = fm::launch_attn_dq(s->dtype, a, hs, g_bwd_end);
   }
   return hip_status(e);
@@ -299,6 +310,14 @@ int32_t flashmask_classify(const int32_t* LTS, const int32_t* LTE, const int32_t
   if (e == hipSuccess)
     e = fm::launch_classify(mm, (int32_t)n_kb, nq, BM, cls, qcnt, qlist, kcnt, klist, hs);
   return hip_status(e);
+}
+
+int32_t flashmask_block_order(const int32_t* cnt, int32_t n, int32_t n_other, int32_t* order,
+                              void* stream) {
+  if (!cnt || !order) return FM_ERR_NULL;
+  if (n < 1 || n_other < 0) return FM_ERR_SHAPE;
+  if (!aligned(cnt, 4) || !aligned(order, 4)) return FM_ERR_ALIGN;
+  return hip_status(fm::launch_block_order(cnt, n, n_other, order, static_cast<hipStream_t>(stream)));
 }
 
 int32_t flashmask_set_profile_events(void* fwd_begin, void* fwd_end, void* bwd_begin,

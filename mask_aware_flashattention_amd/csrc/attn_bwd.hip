@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   const int n_kb = (a.nk + C::BN - 1) / C::BN;
   const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
   const int bh = work / n_kb;
-  const int kb = n_kb - 1 - (work % n_kb);
+  const int kb = a.order[work % n_kb];
   const int key = kb * C::BN + w * 32 + l32;  // this lane's key (a column of S)
   const bool key_ok = key < a.nk;
 

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   const int n_qb = (a.nq + C::BM - 1) / C::BM;
   const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
   const int bh = work / n_qb;
-  const int qb = n_qb - 1 - (work % n_qb);
+  const int qb = a.order[work % n_qb];
 
   const T* __restrict__ Qp = static_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
   const T* __restrict__ dOp = static_cast<const T*>(a.dout) + (size_t)bh * a.nq * D;

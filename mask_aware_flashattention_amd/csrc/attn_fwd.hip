@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int bh = work / n_qb;
   // Query blocks are visited last-first: under causal-like masks the later blocks have the
   // longest lists, so the longest work is dispatched first.
-  const int qb = n_qb - 1 - (work % n_qb);
+  const int qb = a.order[work % n_qb];
 
   const T* __restrict__ Qp = static_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
   const T* __restrict__ Kp = static_cast<const T*>(a.k) + (size_t)bh * a.nk * D;

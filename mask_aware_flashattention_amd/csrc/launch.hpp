@@ -25,6 +25,11 @@ hipError_t launch_classify(const int32_t* mm, int32_t n_kb, int32_t nq, int32_t 
                            uint8_t* cls, int32_t* qcnt, int32_t* qlist, int32_t* kcnt,
                            int32_t* klist, hipStream_t stream);
 
+// Block indices 0..n-1 ordered by cnt[i], largest first (order must hold n entries); n_other
+// bounds the counts.
+hipError_t launch_block_order(const int32_t* cnt, int32_t n, int32_t n_other, int32_t* order,
+                              hipStream_t stream);
+
 constexpr int kMaxChunks = 64;
 struct ChunkTable {
   int32_t n_chunks;
@@ -45,6 +50,7 @@ struct FwdArgs {
   float* lse;
   const int32_t* qcnt;
   const int32_t* qlist;
+  const int32_t* order;  // query blocks, longest list first
   int32_t list_stride;  // n_kb
   int32_t B, H, nq, nk;
   float scale;
@@ -68,6 +74,7 @@ struct BwdArgs {
   float* lse2;    // float32 [B,H,nq]: LSE * log2(e), +inf on fully masked rows
   const int32_t* kcnt;
   const int32_t* klist;
+  const int32_t* order;  // key blocks, longest list first
   int32_t list_stride;  // n_qb at the backward tile shape
   int32_t B, H, nq, nk;
   float scale;
@@ -88,6 +95,7 @@ struct DqArgs {
   const float* lse2;
   const int32_t* qcnt;
   const int32_t* qlist;
+  const int32_t* order;  // query blocks, longest list first
   int32_t list_stride;  // n_kb at the forward tile shape
   int32_t B, H, nq, nk;
   float scale;

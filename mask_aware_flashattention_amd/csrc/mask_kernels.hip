@@ -206,6 +206,47 @@ inline int grid_for(int64_t work, int threads, int cap) {
   return (int)(g < cap ? g : cap);
 }
 
+// Longest-first order of blocks by list length: a counting sort on cnt >> shift, in descending
+// order, by one workgroup (blocks whose counts share a bin keep no particular order).  The
+// attention kernels take their work in this order, so long blocks start first and short ones
+// fill the tail of each compute unit's queue (longest-processing-time-first scheduling).
+constexpr int kOrderBins = 2048;
+__global__ __launch_bounds__(1024) void block_order_kernel(const int32_t* __restrict__ cnt,
+                                                           int32_t n, int32_t shift,
+                                                           int32_t* __restrict__ order) {
+  __shared__ int32_t next[kOrderBins];  // histogram, then the next free slot of each bin
+  for (int b = threadIdx.x; b < kOrderBins; b += blockDim.x) next[b] = 0;
+  __syncthreads();
+  auto bin_of = [&](int i) {
+    const int32_t b = cnt[i] >> shift;
+    return b < kOrderBins ? b : kOrderBins - 1;
+  };
+  for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&next[bin_of(i)], 1);
+  __syncthreads();
+  // Exclusive scan over bins from the highest down, by the first wave: lane l owns the 32 bins
+  // kOrderBins-1-32l down to kOrderBins-32-32l.
+  if (threadIdx.x < kWave) {
+    constexpr int PER = kOrderBins / kWave;
+    const int top = kOrderBins - 1 - PER * (int)threadIdx.x;
+    int32_t sum = 0;
+    for (int k = 0; k < PER; ++k) sum += next[top - k];
+    int32_t incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int32_t y = __shfl_up(incl, off);
+      if ((int)threadIdx.x >= off) incl += y;
+    }
+    int32_t run = incl - sum;
+    for (int k = 0; k < PER; ++k) {
+      const int32_t c = next[top - k];
+      next[top - k] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) order[atomicAdd(&next[bin_of(i)], 1)] = i;
+}
+
 }  // namespace
 
 hipError_t launch_block_minmax(MaskVecs v, int32_t nk, int32_t BN, int32_t* mm,
@@ -227,6 +268,15 @@ hipError_t launch_classify(const int32_t* mm, int32_t n_kb, int32_t nq, int32_t 
   const int grid = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
   hipLaunchKernelGGL(classify_kernel, dim3(grid), dim3(256), 0, stream, mm, n_kb, nq, BM, n_qb,
                      row_waves, col_waves, cls, qcnt, qlist, kcnt, klist);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_order(const int32_t* cnt, int32_t n, int32_t n_other, int32_t* order,
+                              hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  int32_t shift = 0;
+  while ((n_other >> shift) >= kOrderBins) ++shift;
+  hipLaunchKernelGGL(block_order_kernel, dim3(1), dim3(1024), 0, stream, cnt, n, shift, order);
   return hipGetLastError();
 }
 

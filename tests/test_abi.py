@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -72,12 +72,14 @@ def test_workspace_sizes(lib):
     s = shape()
     n_qb, n_kb = 3, 4      # forward tiles 128 x 64
     r = lambda x: -(-x // 256) * 256
-    assert lib.flashmask_fwd_workspace_bytes(ctypes.byref(s)) == r(32 * n_kb) + r(4 * n_qb) + r(4 * n_qb * n_kb)
+    assert lib.flashmask_fwd_workspace_bytes(ctypes.byref(s)) == (
+        r(32 * n_kb) + r(4 * n_qb) + r(4 * n_qb * n_kb) + r(4 * n_qb))
     n_qb, n_kb = 5, 2      # dK/dV lists at tiles 64 x 128
     f_qb, f_kb = 3, 4      # dQ lists at the forward tiles 128 x 64
     rows = 1 * 2 * 300
     want = (r(32 * n_kb) + r(4 * n_kb) + r(4 * n_qb * n_kb)
-            + r(32 * f_kb) + r(4 * f_qb) + r(4 * f_qb * f_kb) + 2 * r(4 * rows))
+            + r(32 * f_kb) + r(4 * f_qb) + r(4 * f_qb * f_kb)
+            + r(4 * n_kb) + r(4 * f_qb) + 2 * r(4 * rows))
     assert lib.flashmask_bwd_workspace_bytes(ctypes.byref(s)) == want
     assert lib.flashmask_fwd_workspace_bytes(ctypes.byref(shape(d=64))) == 0
     assert lib.flashmask_classify_workspace_bytes(1000, 64) == 512
@@ -171,3 +173,11 @@ def test_classify_checks(lib):
     assert call(kcnt=NUL) == FM_ERR_NULL          # kcnt and klist go together
     assert call(ws_bytes=10) == FM_ERR_WORKSPACE
     assert call(ws=NUL, ws_bytes=1 << 20) == FM_ERR_WORKSPACE
+
+
+def test_block_order_checks(lib):
+    assert lib.flashmask_block_order(NUL, 4, 4, P2, NUL) == FM_ERR_NULL
+    assert lib.flashmask_block_order(P2, 4, 4, NUL, NUL) == FM_ERR_NULL
+    assert lib.flashmask_block_order(P2, 0, 4, P2, NUL) == FM_ERR_SHAPE
+    assert lib.flashmask_block_order(P2, 4, -1, P2, NUL) == FM_ERR_SHAPE
+    assert lib.flashmask_block_order(ctypes.c_void_p(0x100002), 4, 4, P2, NUL) == FM_ERR_ALIGN

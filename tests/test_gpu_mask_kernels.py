@@ -116,3 +116,18 @@ def test_classify_random_vectors_and_tiles(fm, seed):
     got = fm.classify(*[dev_i32(x) for x in v], nq, BM, BN)
     torch.cuda.synchronize()
     compare_classify(got, oracle.classify(*v, nq, BM, BN), BM, BN)
+
+
+@pytest.mark.parametrize("n,n_other", [(1, 1), (300, 100), (5000, 5000), (65536, 1 << 16)])
+def test_block_order_is_longest_first_permutation(fm, n, n_other):
+    # a scheduling aid with no oracle of its own: check the properties the header states
+    r = rng(5, n)
+    cnt = r.integers(0, n_other + 1, size=n).astype(np.int32)
+    cnt[r.integers(0, n, size=min(n, 7))] = n_other  # ties at the maximum
+    order = fm.api.block_order(dev_i32(cnt), n_other).cpu().numpy()
+    assert np.array_equal(np.sort(order), np.arange(n))
+    shift = 0
+    while (n_other >> shift) >= 2048:
+        shift += 1
+    keys = np.minimum(cnt[order] >> shift, 2047)
+    assert np.all(np.diff(keys) <= 0)
