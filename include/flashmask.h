@@ -154,17 +154,17 @@ int32_t flashmask_classify(const int32_t* LTS, const int32_t* LTE, const int32_t
 
 /*
  * Work order of the attention kernels (a scheduling aid; exposed for testing).  Writes to
- * order[0..n) a permutation of 0..n-1 in which the block counts cnt[order[k]] >> s never
- * increase with k, where s is the smallest shift with (n_other >> s) < 2048 (n_other bounds the
- * counts).  Blocks in one bucket come in no particular order.  The forward and both backward
- * kernels take their blocks in this order (longest list first), so that the longest-running
- * workgroups start first; the order changes no result.  "FlashMask-3 ..." (zicq.com summary)
- * names load balance across ranks as a goal; this is its counterpart inside one GPU.
- * cnt, order: device int32 [n], 4-byte aligned.  Errors: FM_ERR_NULL, FM_ERR_SHAPE (n < 1 or
- * n_other < 0), FM_ERR_ALIGN, FM_ERR_HIP.
+ * order[0..n) a permutation of 0..n-1: blocks i go into four buckets by
+ * floor(max(cnt[i], 0) * 4 / (max_k cnt[k] + 1)), the bucket of the largest counts first, and
+ * inside a bucket in descending i.  The forward and both backward kernels take their blocks in
+ * this order (cnt = their list lengths): long blocks start early, and blocks that run together
+ * stay close in the sequence, so they share K / V tiles in cache.  The order changes no result.
+ * "FlashMask-3 ..." (zicq.com summary) names load balance across ranks as a goal; this is its
+ * counterpart inside one GPU.
+ * cnt, order: device int32 [n], 4-byte aligned.  Errors: FM_ERR_NULL, FM_ERR_SHAPE (n < 1),
+ * FM_ERR_ALIGN, FM_ERR_HIP.
  */
-int32_t flashmask_block_order(const int32_t* cnt, int32_t n, int32_t n_other, int32_t* order,
-                              void* stream);
+int32_t flashmask_block_order(const int32_t* cnt, int32_t n, int32_t* order, void* stream);
 
 /*
  * Diagnostic hook for timing the attention kernels alone (a benchmark aid; not needed to use the

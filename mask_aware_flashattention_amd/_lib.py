@@ -40,7 +40,7 @@ SIGNATURES = {
                                    c_p, c_p, c_p, c_p, c_i32p, c_p]),
     "flashmask_classify_workspace_bytes": (ctypes.c_size_t, [c_i32, c_i32]),
     "flashmask_set_profile_events": (c_i32, [c_p, c_p, c_p, c_p]),
-    "flashmask_block_order": (c_i32, [c_p, c_i32, c_i32, c_p, c_p]),
+    "flashmask_block_order": (c_i32, [c_p, c_i32, c_p, c_p]),
     "flashmask_classify": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_p, c_p,
                                    c_p, c_p, c_p, c_p, ctypes.c_size_t, c_p]),
 }

@@ -155,13 +155,14 @@ def classify(lts, lte, uts, ute, nq, BM, BN, *, cls=True, qlists=True, klists=Tr
     return out
 
 
-def block_order(cnt, n_other):
-    """Longest-first work order of the attention kernels for block counts `cnt` (int32 device
-    tensor), counts bounded by n_other; returns an int32 permutation tensor."""
+def block_order(cnt):
+    """Work order of the attention kernels for block counts `cnt` (int32 device tensor): four
+    buckets by count, largest first, descending index inside a bucket; returns an int32
+    permutation tensor."""
     lib = _lib.load()
     if cnt.dtype != torch.int32 or not cnt.is_contiguous():
         raise ValueError("cnt must be a contiguous int32 tensor")
     order = torch.empty_like(cnt)
-    check(lib.flashmask_block_order(_ptr(cnt), cnt.numel(), int(n_other), _ptr(order),
-                                    _stream(cnt.device)), "flashmask_block_order")
+    check(lib.flashmask_block_order(_ptr(cnt), cnt.numel(), _ptr(order), _stream(cnt.device)),
+          "flashmask_block_order")
     return order

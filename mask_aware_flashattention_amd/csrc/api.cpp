@@ -172,7 +172,7 @@ int32_t flashmask_fwd(const fm_shape* s, const void* Q, const void* K, const voi
   if (e == hipSuccess)
     e = fm::launch_classify(mm, (int32_t)g.n_kb, s->nq, t.bm_fwd, nullptr, qcnt, qlist, nullptr,
                             nullptr, hs);
-  if (e == hipSuccess) e = fm::launch_block_order(qcnt, (int32_t)g.n_qb, (int32_t)g.n_kb, order, hs);
+  if (e == hipSuccess) e = fm::launch_block_order(qcnt, (int32_t)g.n_qb, order, hs);
   if (e == hipSuccess) {
     fm::FwdArgs a{Q,     K,     V,     mv,   O,    LSE,  qcnt, qlist, order, (int32_t)g.n_kb,
                   s->B, s->H, s->nq, s->nk, scale};
@@ -234,8 +234,8 @@ int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const voi
   if (e == hipSuccess)
     e = fm::launch_classify(mm_f, (int32_t)gf.n_kb, s->nq, t.bm_fwd, nullptr, qcnt, qlist, nullptr,
                             nullptr, hs);
-  if (e == hipSuccess) e = fm::launch_block_order(kcnt, (int32_t)g.n_kb, (int32_t)g.n_qb, korder, hs);
-  if (e == hipSuccess) e = fm::launch_block_order(qcnt, (int32_t)gf.n_qb, (int32_t)gf.n_kb, qorder, hs);
+  if (e == hipSuccess) e = fm::launch_block_order(kcnt, (int32_t)g.n_kb, korder, hs);
+  if (e == hipSuccess) e = fm::launch_block_order(qcnt, (int32_t)gf.n_qb, qorder, hs);
   if (e == hipSuccess) {
     fm::BwdArgs a{Q,     K,    V,      O,    dO,   LSE,  mv,   dK, dV, delta, lse2, kcnt, klist,
                   korder, (int32_t)g.n_qb, s->B, s->H, s->nq, s->nk, scale};
@@ -312,12 +312,11 @@ int32_t flashmask_classify(const int32_t* LTS, const int32_t* LTE, const int32_t
   return hip_status(e);
 }
 
-int32_t flashmask_block_order(const int32_t* cnt, int32_t n, int32_t n_other, int32_t* order,
-                              void* stream) {
+int32_t flashmask_block_order(const int32_t* cnt, int32_t n, int32_t* order, void* stream) {
   if (!cnt || !order) return FM_ERR_NULL;
-  if (n < 1 || n_other < 0) return FM_ERR_SHAPE;
+  if (n < 1) return FM_ERR_SHAPE;
   if (!aligned(cnt, 4) || !aligned(order, 4)) return FM_ERR_ALIGN;
-  return hip_status(fm::launch_block_order(cnt, n, n_other, order, static_cast<hipStream_t>(stream)));
+  return hip_status(fm::launch_block_order(cnt, n, order, static_cast<hipStream_t>(stream)));
 }
 
 int32_t flashmask_set_profile_events(void* fwd_begin, void* fwd_end, void* bwd_begin,

@@ -25,10 +25,9 @@ hipError_t launch_classify(const int32_t* mm, int32_t n_kb, int32_t nq, int32_t 
                            uint8_t* cls, int32_t* qcnt, int32_t* qlist, int32_t* kcnt,
                            int32_t* klist, hipStream_t stream);
 
-// Block indices 0..n-1 ordered by cnt[i], largest first (order must hold n entries); n_other
-// bounds the counts.
-hipError_t launch_block_order(const int32_t* cnt, int32_t n, int32_t n_other, int32_t* order,
-                              hipStream_t stream);
+// Block indices 0..n-1 in four buckets by cnt[i], the bucket of the largest counts first,
+// descending index order inside a bucket (order must hold n entries).
+hipError_t launch_block_order(const int32_t* cnt, int32_t n, int32_t* order, hipStream_t stream);
 
 constexpr int kMaxChunks = 64;
 struct ChunkTable {

@@ -206,45 +206,82 @@ inline int grid_for(int64_t work, int threads, int cap) {
   return (int)(g < cap ? g : cap);
 }
 
-// Longest-first order of blocks by list length: a counting sort on cnt >> shift, in descending
-// order, by one workgroup (blocks whose counts share a bin keep no particular order).  The
-// attention kernels take their work in this order, so long blocks start first and short ones
-// fill the tail of each compute unit's queue (longest-processing-time-first scheduling).
-constexpr int kOrderBins = 2048;
-__global__ __launch_bounds__(1024) void block_order_kernel(const int32_t* __restrict__ cnt,
-                                                           int32_t n, int32_t shift,
-                                                           int32_t* __restrict__ order) {
-  __shared__ int32_t next[kOrderBins];  // histogram, then the next free slot of each bin
-  for (int b = threadIdx.x; b < kOrderBins; b += blockDim.x) next[b] = 0;
+// Work order of the attention kernels: blocks go into kOrderBuckets buckets by list length
+// (bucket b holds counts c with floor(c * kOrderBuckets / (max + 1)) = b), the bucket of the
+// longest lists first, so that long workgroups start early and short ones fill the tail of each
+// compute unit's queue.  Inside a bucket the blocks keep descending index order, so workgroups
+// that run at the same time stay close in the sequence and share K / V tiles in the L2 cache.
+// One workgroup, deterministic: thread t owns a contiguous run of the descending index sequence
+// and a scan over threads gives each of its blocks its slot.
+constexpr int kOrderBuckets = 4;
+constexpr int kOrderThreads = 1024;
+__global__ __launch_bounds__(kOrderThreads) void block_order_kernel(const int32_t* __restrict__ cnt,
+                                                                    int32_t n,
+                                                                    int32_t* __restrict__ order) {
+  constexpr int kWaves = kOrderThreads / kWave;
+  __shared__ int32_t wmax[kWaves];
+  __shared__ int32_t slot[kOrderBuckets][kOrderThreads];  // per-thread counts, then first slots
+  __shared__ int32_t total[kOrderBuckets];
+  const int t = threadIdx.x, lane = t & (kWave - 1), wv = t >> 6;
+  int32_t mx = 0;
+  for (int i = t; i < n; i += kOrderThreads) mx = cnt[i] > mx ? cnt[i] : mx;
+  mx = wave_reduce(mx, MaxOp());
+  if (lane == 0) wmax[wv] = mx;
   __syncthreads();
-  auto bin_of = [&](int i) {
-    const int32_t b = cnt[i] >> shift;
-    return b < kOrderBins ? b : kOrderBins - 1;
-  };
-  for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&next[bin_of(i)], 1);
+  mx = 0;
+  for (int k = 0; k < kWaves; ++k) mx = wmax[k] > mx ? wmax[k] : mx;
+  const int64_t span = (int64_t)mx + 1;
+  auto bucket_of = [&](int32_t c) { return (int)(((int64_t)(c > 0 ? c : 0) * kOrderBuckets) / span); };
+  const int chunk = (n + kOrderThreads - 1) / kOrderThreads;
+  const int p0 = t * chunk < n ? t * chunk : n;
+  const int p1 = p0 + chunk < n ? p0 + chunk : n;
+  int32_t mine[kOrderBuckets] = {};
+  for (int p = p0; p < p1; ++p) {
+    const int b = bucket_of(cnt[n - 1 - p]);
+#pragma unroll
+    for (int k = 0; k < kOrderBuckets; ++k) mine[k] += (b == k);
+  }
+#pragma unroll
+  for (int k = 0; k < kOrderBuckets; ++k) slot[k][t] = mine[k];
   __syncthreads();
-  // Exclusive scan over bins from the highest down, by the first wave: lane l owns the 32 bins
-  // kOrderBins-1-32l down to kOrderBins-32-32l.
-  if (threadIdx.x < kWave) {
-    constexpr int PER = kOrderBins / kWave;
-    const int top = kOrderBins - 1 - PER * (int)threadIdx.x;
+  // exclusive scan over threads, wave b for bucket b (kOrderThreads / kWave entries per lane)
+  if (wv < kOrderBuckets) {
+    constexpr int PER = kOrderThreads / kWave;
+    int32_t* row = slot[wv];
     int32_t sum = 0;
-    for (int k = 0; k < PER; ++k) sum += next[top - k];
+    for (int k = 0; k < PER; ++k) sum += row[lane * PER + k];
     int32_t incl = sum;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
       const int32_t y = __shfl_up(incl, off);
-      if ((int)threadIdx.x >= off) incl += y;
+      if (lane >= off) incl += y;
     }
     int32_t run = incl - sum;
     for (int k = 0; k < PER; ++k) {
-      const int32_t c = next[top - k];
-      next[top - k] = run;
+      const int32_t c = row[lane * PER + k];
+      row[lane * PER + k] = run;
       run += c;
     }
+    if (lane == kWave - 1) total[wv] = incl;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) order[atomicAdd(&next[bin_of(i)], 1)] = i;
+  int32_t pos[kOrderBuckets];
+  int32_t base = 0;
+#pragma unroll
+  for (int k = kOrderBuckets - 1; k >= 0; --k) {
+    pos[k] = base + slot[k][t];
+    base += total[k];
+  }
+  for (int p = p0; p < p1; ++p) {
+    const int i = n - 1 - p;
+    const int b = bucket_of(cnt[i]);
+    int32_t at = 0;
+#pragma unroll
+    for (int k = 0; k < kOrderBuckets; ++k) {
+      if (b == k) at = pos[k]++;
+    }
+    order[at] = i;
+  }
 }
 
 }  // namespace
@@ -271,12 +308,9 @@ hipError_t launch_classify(const int32_t* mm, int32_t n_kb, int32_t nq, int32_t 
   return hipGetLastError();
 }
 
-hipError_t launch_block_order(const int32_t* cnt, int32_t n, int32_t n_other, int32_t* order,
-                              hipStream_t stream) {
+hipError_t launch_block_order(const int32_t* cnt, int32_t n, int32_t* order, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  int32_t shift = 0;
-  while ((n_other >> shift) >= kOrderBins) ++shift;
-  hipLaunchKernelGGL(block_order_kernel, dim3(1), dim3(1024), 0, stream, cnt, n, shift, order);
+  hipLaunchKernelGGL(block_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, cnt, n, order);
   return hipGetLastError();
 }
 

@@ -176,8 +176,7 @@ def test_classify_checks(lib):
 
 
 def test_block_order_checks(lib):
-    assert lib.flashmask_block_order(NUL, 4, 4, P2, NUL) == FM_ERR_NULL
-    assert lib.flashmask_block_order(P2, 4, 4, NUL, NUL) == FM_ERR_NULL
-    assert lib.flashmask_block_order(P2, 0, 4, P2, NUL) == FM_ERR_SHAPE
-    assert lib.flashmask_block_order(P2, 4, -1, P2, NUL) == FM_ERR_SHAPE
-    assert lib.flashmask_block_order(ctypes.c_void_p(0x100002), 4, 4, P2, NUL) == FM_ERR_ALIGN
+    assert lib.flashmask_block_order(NUL, 4, P2, NUL) == FM_ERR_NULL
+    assert lib.flashmask_block_order(P2, 4, NUL, NUL) == FM_ERR_NULL
+    assert lib.flashmask_block_order(P2, 0, P2, NUL) == FM_ERR_SHAPE
+    assert lib.flashmask_block_order(ctypes.c_void_p(0x100002), 4, P2, NUL) == FM_ERR_ALIGN

@@ -118,16 +118,13 @@ def test_classify_random_vectors_and_tiles(fm, seed):
     compare_classify(got, oracle.classify(*v, nq, BM, BN), BM, BN)
 
 
-@pytest.mark.parametrize("n,n_other", [(1, 1), (300, 100), (5000, 5000), (65536, 1 << 16)])
-def test_block_order_is_longest_first_permutation(fm, n, n_other):
-    # a scheduling aid with no oracle of its own: check the properties the header states
+@pytest.mark.parametrize("n,top", [(1, 1), (300, 100), (5000, 5000), (65536, 1 << 16), (77, 0)])
+def test_block_order_matches_its_definition(fm, n, top):
+    # a scheduling aid, not part of the method: compared with its definition in the header
     r = rng(5, n)
-    cnt = r.integers(0, n_other + 1, size=n).astype(np.int32)
-    cnt[r.integers(0, n, size=min(n, 7))] = n_other  # ties at the maximum
-    order = fm.api.block_order(dev_i32(cnt), n_other).cpu().numpy()
-    assert np.array_equal(np.sort(order), np.arange(n))
-    shift = 0
-    while (n_other >> shift) >= 2048:
-        shift += 1
-    keys = np.minimum(cnt[order] >> shift, 2047)
-    assert np.all(np.diff(keys) <= 0)
+    cnt = r.integers(0, top + 1, size=n).astype(np.int32)
+    cnt[r.integers(0, n, size=min(n, 7))] = top  # ties at the maximum
+    order = fm.api.block_order(dev_i32(cnt)).cpu().numpy()
+    bucket = (np.maximum(cnt, 0).astype(np.int64) * 4) // (int(cnt.max()) + 1)
+    want = [i for b in (3, 2, 1, 0) for i in range(n - 1, -1, -1) if bucket[i] == b]
+    assert np.array_equal(order, np.asarray(want))
