@@ -15,6 +15,7 @@ from .flashmask_oracle import (  # noqa: F401
     attention_bwd,
     block_minmax,
     classify,
+    prune_chunks,
     localize,
     localize_chunks_check,
 )

@@ -277,6 +277,23 @@ def classify(LTS, LTE, UTS, UTE, nq: int, BM: int, BN: int):
     }
 
 
+def prune_chunks(LTS, LTE, UTS, UTE, n_local: int, BM: int, chunk: int):
+    """Which key/value chunks a context-parallel rank needs ([explainer, across-ranks
+    paragraph]: the forward all-gather skips key-value chunks that are fully masked; [abstract]:
+    mask-driven communication pruning).
+
+    The vectors are the rank's localised ones (values in local row numbering, indexed by global
+    key).  Reading: the same min/max tile classification as inside one GPU, with key blocks of
+    `chunk` keys (the unit the all-gather moves) and query blocks of BM local rows.  Returns, per
+    chunk c, the number of BM-row blocks of the rank's rows whose tile in column c is not fully
+    masked (int64 [ceil(nk / chunk)]); 0 means the rank never needs chunk c.  With BM equal to the
+    rank's chunk length every query block is one contiguous run of global rows, and the rule is
+    then exact for the causal, document and sliding-window families.
+    """
+    cls = classify(LTS, LTE, UTS, UTE, n_local, BM, chunk)["cls"]
+    return (cls != 0).sum(axis=0).astype(np.int64)
+
+
 # --------------------------------------------------------------------------------------------
 # rank-local mask: clip-shift-max
 # --------------------------------------------------------------------------------------------

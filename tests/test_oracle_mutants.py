@@ -1,6 +1,6 @@
 """Planted mistakes: each mutant below is a plausible slip in the oracle (a closed interval, a
 dropped stretch, a missing scale, a dropped term, a wrong operand, an unsound bound, an
-off-by-one block, the two-sided clamp).  Each must be caught by at least one of the pins in the
+off-by-one block, the two-sided clamp, a prune list that drops partly masked chunks).  Each must be caught by at least one of the pins in the
 oracle's tests, which shows the pins constrain the oracle rather than restate it.  The mistakes
 are planted in the oracle only, on the CPU."""
 
@@ -12,10 +12,11 @@ import oracle.flashmask_oracle as fo
 from tests import test_oracle_attention as ta
 from tests import test_oracle_classify as tc
 from tests import test_oracle_localize as tl
+from tests import test_oracle_prune as tp
 from tests import test_workloads as tw
 
 _orig = {n: getattr(fo, n) for n in ("dense_mask", "fwd_rows", "bwd_rows", "block_minmax",
-                                     "classify", "localize")}
+                                     "classify", "localize", "prune_chunks")}
 
 
 def _patch(monkeypatch, name, fn):
@@ -104,6 +105,12 @@ def localize_two_sided(LTS, LTE, UTS, UTE, chunk_start, chunk_len, nq_global):
     return ell(LTS), ell(LTE), ell(UTS), ell(UTE), int(L.sum())
 
 
+def prune_counts_unmasked_only(LTS, LTE, UTS, UTE, n_local, BM, chunk):
+    # counts only tiles with no masked entry, so chunks seen through partial tiles are pruned
+    cls = fo.classify(LTS, LTE, UTS, UTE, n_local, BM, chunk)["cls"]
+    return (cls == 2).sum(axis=0).astype(np.int64)
+
+
 def _doc_seed0():
     tw.test_document(3)
     tw.test_sliding_window(40, 7)
@@ -129,6 +136,8 @@ MUTANTS = [
     ("block_minmax", minmax_off_by_one, tc.test_block_minmax_against_numpy_reduce),
     ("classify", classify_unsound, lambda: [tc.test_sound_on_arbitrary_vectors(s) for s in range(40)]),
     ("localize", localize_two_sided, lambda: [tl.test_theorem1_dense(s) for s in range(60)]),
+    ("prune_chunks", prune_counts_unmasked_only,
+     lambda: [tp.test_pruned_chunks_are_fully_masked(s) for s in range(40)]),
 ]
 
 
