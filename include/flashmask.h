@@ -153,6 +153,29 @@ int32_t flashmask_classify(const int32_t* LTS, const int32_t* LTE, const int32_t
                            int32_t* klist, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Key/value chunk prune list for a context-parallel rank: the decision half of mask-driven
+ * communication pruning.  "FlashMask-3 sends each GPU its mask ..." (learnaivisually.com),
+ * across-ranks paragraph: the forward all-gather skips key-value chunks that are fully masked;
+ * "FlashMask-3: Efficient and Expressive Mask-Aware Distributed Attention", abstract.
+ * Inputs: the rank's localised vectors (flashmask_localize; device int32 [nk], values in local
+ * row numbering, indexed by global key), n_local local rows, query blocks of BM local rows and
+ * key chunks of `chunk` keys (the unit the all-gather moves).
+ * Output live (device int32 [ceil(nk/chunk)], overwritten): for chunk c, the number of BM-row
+ * blocks whose tile in column c is not fully masked under the min/max classification rule of
+ * flashmask_classify; 0 means the rank never needs chunk c.  With BM equal to the rank's chunk
+ * length each query block is one contiguous run of global rows and the rule is exact for the
+ * causal, document and sliding-window families.
+ * ws: at least flashmask_prune_workspace_bytes(nk, n_local, BM, chunk) device bytes, 4-byte
+ * aligned (block min/max and the column lists).  Deterministic.  Errors: FM_ERR_NULL,
+ * FM_ERR_SHAPE (a size < 1, or too many tiles), FM_ERR_ALIGN, FM_ERR_WORKSPACE, FM_ERR_HIP.
+ */
+size_t flashmask_prune_workspace_bytes(int32_t nk, int32_t n_local, int32_t BM, int32_t chunk);
+int32_t flashmask_prune_chunks(const int32_t* LTS, const int32_t* LTE, const int32_t* UTS,
+                               const int32_t* UTE, int32_t nk, int32_t n_local, int32_t BM,
+                               int32_t chunk, int32_t* live, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
  * Work order of the attention kernels (a scheduling aid; exposed for testing).  Writes to
  * order[0..n) a permutation of 0..n-1: blocks i go into four buckets by
  * floor(max(cnt[i], 0) * 4 / (max_k cnt[k] + 1)), the bucket of the largest counts first, and

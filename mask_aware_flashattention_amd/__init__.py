@@ -6,11 +6,13 @@ in ``include/flashmask.h``); this package is its thin torch binding.
 
 from ._lib import FlashMaskError, load as load_library  # noqa: F401
 from .api import (  # noqa: F401
+    block_order,
     bwd,
     bwd_workspace_bytes,
     classify,
     fwd,
     fwd_workspace_bytes,
     localize,
+    prune_chunks,
     tile_sizes,
 )

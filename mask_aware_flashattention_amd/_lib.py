@@ -41,6 +41,9 @@ SIGNATURES = {
     "flashmask_classify_workspace_bytes": (ctypes.c_size_t, [c_i32, c_i32]),
     "flashmask_set_profile_events": (c_i32, [c_p, c_p, c_p, c_p]),
     "flashmask_block_order": (c_i32, [c_p, c_i32, c_p, c_p]),
+    "flashmask_prune_workspace_bytes": (ctypes.c_size_t, [c_i32, c_i32, c_i32, c_i32]),
+    "flashmask_prune_chunks": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_p, c_p,
+                                       ctypes.c_size_t, c_p]),
     "flashmask_classify": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_p, c_p,
                                    c_p, c_p, c_p, c_p, ctypes.c_size_t, c_p]),
 }

@@ -166,3 +166,18 @@ def block_order(cnt):
     check(lib.flashmask_block_order(_ptr(cnt), cnt.numel(), _ptr(order), _stream(cnt.device)),
           "flashmask_block_order")
     return order
+
+
+def prune_chunks(lts, lte, uts, ute, n_local, BM, chunk):
+    """Per key chunk of `chunk` keys, the number of BM-row blocks of the rank's n_local rows whose
+    tile is not fully masked (0: the rank never needs the chunk), from localised vectors."""
+    lib = _lib.load()
+    nk = lts.numel()
+    _vectors(lts, lte, uts, ute, nk)
+    dev = lts.device
+    live = torch.empty(-(-nk // chunk), dtype=torch.int32, device=dev)
+    ws = _workspace(lib.flashmask_prune_workspace_bytes(nk, n_local, BM, chunk), dev)
+    check(lib.flashmask_prune_chunks(_ptr(lts), _ptr(lte), _ptr(uts), _ptr(ute), nk, int(n_local),
+                                     int(BM), int(chunk), _ptr(live), _ptr(ws), ws.numel(),
+                                     _stream(dev)), "flashmask_prune_chunks")
+    return live

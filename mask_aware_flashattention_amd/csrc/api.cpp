@@ -312,6 +312,39 @@ int32_t flashmask_classify(const int32_t* LTS, const int32_t* LTE, const int32_t
   return hip_status(e);
 }
 
+size_t flashmask_prune_workspace_bytes(int32_t nk, int32_t n_local, int32_t BM, int32_t chunk) {
+  if (nk < 1 || n_local < 1 || BM < 1 || chunk < 1) return 0;
+  const int64_t n_qb = ceil_div(n_local, BM), n_c = ceil_div(nk, chunk);
+  if (n_qb * n_c > kMaxListEntries) return 0;
+  return round_up(sizeof(int32_t) * 8 * (size_t)n_c) + round_up(sizeof(int32_t) * (size_t)(n_qb * n_c));
+}
+
+int32_t flashmask_prune_chunks(const int32_t* LTS, const int32_t* LTE, const int32_t* UTS,
+                               const int32_t* UTE, int32_t nk, int32_t n_local, int32_t BM,
+                               int32_t chunk, int32_t* live, void* ws, size_t ws_bytes,
+                               void* stream) {
+  int32_t st = check_vectors(LTS, LTE, UTS, UTE);
+  if (st != FM_OK) return st;
+  if (!live) return FM_ERR_NULL;
+  if (nk < 1 || n_local < 1 || BM < 1 || chunk < 1) return FM_ERR_SHAPE;
+  const int64_t n_qb = ceil_div(n_local, BM), n_c = ceil_div(nk, chunk);
+  if (n_qb * n_c > kMaxListEntries || n_qb > 0x7fffffffLL / 4 || n_c > 0x7fffffffLL / 4)
+    return FM_ERR_SHAPE;
+  if (!aligned(live, 4)) return FM_ERR_ALIGN;
+  const size_t need = flashmask_prune_workspace_bytes(nk, n_local, BM, chunk);
+  if (!ws || ws_bytes < need) return FM_ERR_WORKSPACE;
+  if (!aligned(ws, 4)) return FM_ERR_ALIGN;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  int32_t* mm = static_cast<int32_t*>(ws);
+  int32_t* klist = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + round_up(sizeof(int32_t) * 8 * (size_t)n_c));
+  const fm::MaskVecs mv{LTS, LTE, UTS, UTE};
+  // The column-orientation count of the tile classification at (BM, chunk) is the answer.
+  hipError_t e = fm::launch_block_minmax(mv, nk, chunk, mm, hs);
+  if (e == hipSuccess)
+    e = fm::launch_classify(mm, (int32_t)n_c, n_local, BM, nullptr, nullptr, nullptr, live, klist, hs);
+  return hip_status(e);
+}
+
 int32_t flashmask_block_order(const int32_t* cnt, int32_t n, int32_t* order, void* stream) {
   if (!cnt || !order) return FM_ERR_NULL;
   if (n < 1) return FM_ERR_SHAPE;

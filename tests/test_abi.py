@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -180,3 +180,19 @@ def test_block_order_checks(lib):
     assert lib.flashmask_block_order(P2, 4, NUL, NUL) == FM_ERR_NULL
     assert lib.flashmask_block_order(P2, 0, P2, NUL) == FM_ERR_SHAPE
     assert lib.flashmask_block_order(ctypes.c_void_p(0x100002), 4, P2, NUL) == FM_ERR_ALIGN
+
+
+def test_prune_checks(lib):
+    assert lib.flashmask_prune_workspace_bytes(1000, 300, 100, 64) == 512 + 256  # 16 chunks, 3 blocks
+    assert lib.flashmask_prune_workspace_bytes(0, 300, 100, 64) == 0
+
+    def call(vec=P, live=P2, nk=1000, n_local=300, BM=100, chunk=64, ws=P, ws_bytes=1 << 20):
+        return lib.flashmask_prune_chunks(vec, vec, vec, vec, nk, n_local, BM, chunk, live, ws,
+                                          ws_bytes, NUL)
+    assert call(vec=NUL) == FM_ERR_NULL
+    assert call(live=NUL) == FM_ERR_NULL
+    for bad in (dict(nk=0), dict(n_local=0), dict(BM=0), dict(chunk=-3)):
+        assert call(**bad) == FM_ERR_SHAPE, bad
+    assert call(live=ctypes.c_void_p(0x200002)) == FM_ERR_ALIGN
+    assert call(ws_bytes=767) == FM_ERR_WORKSPACE
+    assert call(ws=NUL) == FM_ERR_WORKSPACE
