@@ -1,9 +1,11 @@
 """Benchmark: mask-aware attention forward + backward on one MI355X.
 
 One step = one pass of the whole path over the workload: flashmask_fwd (block min/max,
-classification, attention forward) then flashmask_bwd (block min/max, classification,
-preprocess, attention backward, dQ conversion); for the context-parallel share the step also
-starts with flashmask_localize.  Inputs are seeded synthetic tensors resident in HBM before the
+classification, block order, attention forward) then flashmask_bwd (the same at both tile
+shapes, preprocess, dK/dV kernel, dQ kernel); for the context-parallel share the step also
+starts with flashmask_localize.  ``--workload cp16`` times all 16 ranks of the 128K
+context-parallel share one after another on this GPU (per rank: localize, prune list, forward,
+backward on its 8192 rows against all 131072 keys) beside one global call.  Inputs are seeded synthetic tensors resident in HBM before the
 timed region.  Throughput counts unmasked score entries only: 4*d FLOPs per entry forward,
 10*d backward.
 
@@ -113,6 +115,70 @@ def cpu_baseline(w, vectors, tensors, mask_rows, seconds: float):
     }
 
 
+def cp_emulation(args):
+    """All ranks of the 16-way context-parallel 128K document share, one after another on one
+    GPU; value = the global problem's unmasked FLOPs / time of the 16 rank steps."""
+    import numpy as np
+    import torch
+
+    import mask_aware_flashattention_amd as fm
+    from workloads import configs
+
+    fm.load_library()
+    dev = torch.device("cuda:0")
+    w = configs.WORKLOADS["c5"]
+    R, L = configs.C5_DEGREE, configs.C5_CHUNK
+    n, H, d = 2 * R * L, w.H, w.d
+    gv = configs.global_mask(w)
+    gdev = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in gv]
+    U = unmasked_entries(gv, n)
+    flop = 14 * d * H * U
+    g = torch.Generator(device=dev).manual_seed(20261203)
+    q, k, v, do = (torch.randn((1, H, n, d), generator=g, device=dev).to(torch.bfloat16)
+                   for _ in range(4))
+    ranks = []
+    for r in range(R):
+        starts, lens = [r * L, (2 * R - 1 - r) * L], [L, L]
+        rows = torch.cat([torch.arange(a, a + b, device=dev) for a, b in zip(starts, lens)])
+        ranks.append((starts, lens, q.index_select(2, rows).contiguous(),
+                      do.index_select(2, rows).contiguous()))
+
+    def rank_steps():
+        for starts, lens, q_l, do_l in ranks:
+            lv = fm.localize(*gdev, starts, lens, n)
+            fm.prune_chunks(*lv[:4], lv[4], L, L)
+            o_l, lse_l = fm.fwd(q_l, k, v, *lv[:4])
+            fm.bwd(q_l, k, v, o_l, do_l, lse_l, *lv[:4])
+
+    def global_step():
+        o, lse = fm.fwd(q, k, v, *gdev)
+        fm.bwd(q, k, v, o, do, lse, *gdev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    ms_ranks = timed(rank_steps)
+    ms_global = timed(global_step)
+    print(json.dumps({
+        "metric": METRIC, "value": round(flop / (ms_ranks * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_ranks, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "cp16: 16 ranks x 8192 rows of the 131072-row 24-document mask, "
+                               "run one after another", "B": 1, "H": H, "n": n, "d": d,
+                   "unmasked_per_head": U, "flop_fwd_plus_bwd": flop},
+        "global_call_ms": round(ms_global, 4),
+        "global_call_tflops": round(flop / (ms_global * 1e-3) / 1e12, 2),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +206,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload == "cp16":
+        cp_emulation(args)
+        return
     lib = fm.load_library()
     dev = torch.device("cuda:0")
     w = configs.WORKLOADS[args.workload]
