@@ -1,4 +1,4 @@
-// Mask-aware attention backward for gfx950.
+// Mask-aware attention backward for gfx950: preprocess and the dK / dV kernel.
 //
 // The pages report the backward's speed ("FlashMask-3 ..." zicq.com summary, end-to-end
 // paragraph) but do not describe it; this is the standard recompute-from-LSE backward restricted
@@ -7,15 +7,19 @@
 // tile-classification paragraph).
 //
 //   K4 bwd_pre:  D_i = sum_d dO_id O_id and LSE_i * log2(e) per query row.
-//   K5 bwd_dkdv: one workgroup per key block of BN = 128 keys (4 waves x 32 keys).  K and V rows
-//                of the wave's keys stay in registers (B operands of S = Q K^T and dP = dO V^T)
-//                and dK^T, dV^T accumulate in registers.  The workgroup walks the query blocks
-//                (BM = 64 rows) of its list.  Per tile: S, dP on 32x32 MFMAs with the query rows
-//                loaded in a permuted order so the accumulators double as operands;
-//                P = exp2(S*scale*log2e - LSE*log2e) (0 in masked entries); dS = P (dP - D);
-//                dV^T += dO^T P and dK^T += Q^T dS with the transposed operands read from the
-//                row-major Q / dO tiles by the gfx950 LDS transpose read.  Q / dO tiles go
-//                straight from HBM into LDS, double-buffered, one workgroup barrier per tile.
+//   K5 dK / dV:  one workgroup of 8 waves per key block of BN = 128 keys: 4 key groups of 32
+//                keys, and per key group a pair of waves on one SIMD that split the work:
+//                  the P wave keeps K rows in registers, computes S = Q K^T, P = exp2(S*scale*
+//                  log2e - LSE*log2e) (0 where masked) and accumulates dV^T += dO^T P;
+//                  the dS wave keeps V rows, computes dP = dO V^T, takes P from the P wave
+//                  through LDS, forms dS = P (dP - D) and accumulates dK^T += Q^T dS.
+//                Each wave then needs under 256 registers, so two run on every SIMD and one's
+//                elementwise work overlaps the other's matrix products.  The workgroup walks
+//                the query blocks (BM = 64 rows) of its list in 32-row units; Q and dO rows
+//                are A operands read from LDS in a permuted row order so the accumulators
+//                double as operands, Q^T and dO^T come from the gfx950 LDS transpose read.
+//                Tiles are staged global -> registers -> LDS one tile ahead, double-buffered;
+//                one workgroup barrier per unit (P handed over) also publishes the next tile.
 //   dQ comes from the query-stationary kernel in attn_bwd_dq.hip, so no float32 atomics are
 //   needed and every gradient is deterministic.
 #include <math.h>
@@ -31,16 +35,20 @@ namespace {
 
 template <typename T, int D>
 struct BwdTile {
-  static constexpr int BN = 128, BM = 64, NT = 256;
+  static constexpr int BN = 128, BM = 64, NT = 512;  // 8 waves: 4 key groups x 2 roles
   static constexpr int KPL = Elem<T>::KPL, KSTEP = 2 * KPL;
   static constexpr int CH = 16 / (int)sizeof(T);
-  static constexpr int CPR = D / CH;               // 16-byte chunks per Q / dO / K row
+  static constexpr int CPR = D / CH;  // 16-byte chunks per Q / dO / K row
   static constexpr int ROW_BYTES = D * (int)sizeof(T);
   static constexpr int NDB = D / 32;
   static constexpr int QK_STEPS = D / KSTEP;
+  static constexpr int US = 32 / KSTEP;  // k-steps over a unit's 32 queries
   static constexpr int TILE_BYTES = BM * ROW_BYTES;
+  static constexpr int BUF_BYTES = 2 * TILE_BYTES + 2 * BM * (int)sizeof(float);  // Q|dO|LSE2|D
+  static constexpr int XCH_BYTES = 4 * 16 * 64 * (int)sizeof(float);  // one unit's P, 4 groups
+  static constexpr int SMEM = 2 * BUF_BYTES + 2 * XCH_BYTES;
   static_assert(CPR == 16, "tile loads assume 256-byte rows");
-  static_assert(BM * ROW_BYTES == 16 * 1024, "16 blocks of 1 KiB per tile");
+  static_assert(TILE_BYTES == 16 * 1024, "16 blocks of 1 KiB per tile");
 };
 
 struct MaskRegs {
@@ -48,27 +56,30 @@ struct MaskRegs {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   using C = BwdTile<T, D>;
   using E = Elem<T>;
   using frag = typename E::frag;
-  constexpr int KPL = C::KPL, KSTEP = C::KSTEP;
+  constexpr int KPL = C::KPL, KSTEP = C::KSTEP, US = C::US;
 
-  // LDS: three tile buffers [Q | dO | LSE2 | D].
-  constexpr int BUF_BYTES = 2 * C::TILE_BYTES + 2 * C::BM * (int)sizeof(float);
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  auto bufp = [&](int b) -> unsigned char* { return smem + b * BUF_BYTES; };
-  auto rowsp = [&](int b) -> float* { return reinterpret_cast<float*>(smem + b * BUF_BYTES + 2 * C::TILE_BYTES); };
+  auto bufp = [&](int b) -> unsigned char* { return smem + b * C::BUF_BYTES; };
+  auto rowsp = [&](int b) -> float* {
+    return reinterpret_cast<float*>(smem + b * C::BUF_BYTES + 2 * C::TILE_BYTES);
+  };
+  float* xch = reinterpret_cast<float*>(smem + 2 * C::BUF_BYTES);  // [2 units][4 groups][4][64][4]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int kg = wv & 3;                                     // key group
+  const bool dsw = wv >= 4;                                  // the dS wave of the pair
 
   const int n_kb = (a.nk + C::BN - 1) / C::BN;
   const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
   const int bh = work / n_kb;
   const int kb = a.order[work % n_kb];
-  const int key = kb * C::BN + w * 32 + l32;  // this lane's key (a column of S)
+  const int key = kb * C::BN + kg * 32 + l32;  // this lane's key (a column of S)
   const bool key_ok = key < a.nk;
 
   const T* __restrict__ Qp = static_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
@@ -79,23 +90,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   const float* __restrict__ dlt = a.delta + (size_t)bh * a.nq;
   const buf_rsrc qbuf = make_buf(Qp, (uint32_t)a.nq * C::ROW_BYTES);
   const buf_rsrc dobuf = make_buf(dOp, (uint32_t)a.nq * C::ROW_BYTES);
-  const buf_rsrc kbuf = make_buf(Kp, (uint32_t)a.nk * C::ROW_BYTES);
-  const buf_rsrc vbuf = make_buf(Vp, (uint32_t)a.nk * C::ROW_BYTES);
+  const buf_rsrc kvbuf = make_buf(dsw ? Vp : Kp, (uint32_t)a.nk * C::ROW_BYTES);
   const buf_rsrc lbuf = make_buf(lse2, (uint32_t)a.nq * sizeof(float));
   const buf_rsrc dlbuf = make_buf(dlt, (uint32_t)a.nq * sizeof(float));
 
-  // K and V rows of this lane's key as B operands (k-step s: d = s*KSTEP + g*KPL + 0..KPL).
-  frag kf[C::QK_STEPS], vf[C::QK_STEPS];
+  // K (P wave) or V (dS wave) rows of this lane's key as B operands (k-step s: d = s*KSTEP +
+  // g*KPL + 0..KPL); keys past nk read as zeros.
+  frag bop[C::QK_STEPS];
 #pragma unroll
   for (int s = 0; s < C::QK_STEPS; ++s) {
     const uint32_t off = (uint32_t)key * C::ROW_BYTES + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
-    if constexpr (KPL == 8) {
-      kf[s] = __builtin_bit_cast(frag, buf_load16(kbuf, off, 0));
-      vf[s] = __builtin_bit_cast(frag, buf_load16(vbuf, off, 0));
-    } else {
-      kf[s] = __builtin_bit_cast(frag, buf_load4(kbuf, off, 0));
-      vf[s] = __builtin_bit_cast(frag, buf_load4(vbuf, off, 0));
-    }
+    if constexpr (KPL == 8)
+      bop[s] = __builtin_bit_cast(frag, buf_load16(kvbuf, off, 0));
+    else
+      bop[s] = __builtin_bit_cast(frag, buf_load4(kvbuf, off, 0));
   }
   MaskRegs mk = {0, 0, 0, 0};  // this lane's key; past the last key every row is masked
   if (key_ok) mk = {a.mask.lts[key], a.mask.lte[key], a.mask.uts[key], a.mask.ute[key]};
@@ -107,15 +115,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
   // ---- per-lane LDS byte offsets, constant for the whole kernel ------------------------------
   // Transpose-read lane geometry: lane i of 16-lane block b addresses row k0 + 8*(b/2) + i/4,
   // column m0 + 16*(b%2) + 4*(i%4), and receives rows k0 + 8*(l/32) + 0..3 of column m0 + l%32.
-  // The swizzle depends only on row & 15, so an offset computed for a row below 16 stays valid when a multiple of 16 rows is added as a constant;
-  // every LDS access below is then one of these registers plus an immediate.
+  // The swizzle depends only on row & 15, so an offset computed for a row below 16 stays valid
+  // when a multiple of 16 rows is added as a constant.
   const int tb = lane >> 4, ti = lane & 15;
   const int tr_row = 8 * (tb >> 1) + (ti >> 2);
   const int tr_col = 16 * (tb & 1) + 4 * (ti & 3);
-  constexpr int US = 32 / KSTEP;  // k-steps in a 32-query half
-
-  int off_s[C::QK_STEPS];  // S / dP operand (query row source row, k-step s) of a half
-  int off_tq[C::NDB][2];   // Q^T / dO^T operand rows (tr_row, tr_row + 4), columns 32*db
+  int off_s[C::QK_STEPS];  // row operand (query row source row, k-step s) of a unit
+  int off_tq[C::NDB][2];   // transposed operand rows (tr_row, tr_row + 4), columns 32*db
   {
     const int srow = row_source<KPL>(l32);
 #pragma unroll
@@ -129,9 +135,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
       for (int db = 0; db < C::NDB; ++db) off_tq[db][h] = tile_off<T, 0>(r, 32 * db + cc, C::ROW_BYTES);
     }
   }
+  // The P wave reads Q rows and dO^T, the dS wave dO rows and Q^T.
+  const int row_region = dsw ? C::TILE_BYTES : 0;
+  const int tr_region = dsw ? 0 : C::TILE_BYTES;
 
-  // Operand of a contraction over the rows of a row-major tile (k = tile row): rows
-  // k0 + g*KPL + 0..KPL-1 of this lane's column; `off` = {row tr_row, row tr_row + 4} offsets.
   auto tr_operand = [&](const unsigned char* tile, const int* off, int k0_bytes) -> frag {
     if constexpr (KPL == 8) {
       const s16x4 lo = lds_read_tr16(tile + off[0] + k0_bytes);
@@ -142,52 +149,46 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
     }
   };
 
-  f32x16 dv_acc[C::NDB], dk_acc[C::NDB];
+  f32x16 acc[C::NDB];  // dV^T (P wave) or dK^T (dS wave): row d, column this lane's key
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    dv_acc[db] = f32x16{};
-    dk_acc[db] = f32x16{};
-  }
+  for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
 
   const int cnt = a.kcnt[kb];
   const int32_t* __restrict__ lst = a.klist + (size_t)kb * a.list_stride;
   const float cexp = a.scale * kLog2e;
 
-  // A tile's 64 rows of Q (then dO) are 16 blocks of 1 KiB; wave w moves blocks 4w..4w+3, lane l
-  // the 16-byte slot l of a block, i.e. row 4j + l/16, physical chunk l%16, which holds logical
-  // chunk (l%16) ^ swz_row(row).  Rows past nq read as zeros.  Waves 0 and 1 also move the tile's
-  // LSE2 and D rows.  The loads go to registers first (load_tile) and are written to LDS one
-  // tile later (commit_tile), so no LDS read ever waits on a load in flight.
-  uint4 stq[4], std_[4];
+  // A tile's 64 rows of Q, then of dO, are 32 blocks of 1 KiB; wave w moves blocks 4w..4w+3
+  // (waves 0-3 Q, 4-7 dO), lane l the 16-byte slot l of a block: row 4j + l/16 of its tensor,
+  // physical chunk l%16, which holds logical chunk (l%16) ^ swz_row(row).  Rows past nq read as
+  // zeros.  Waves 0 and 1 also move the tile's LSE2 and D rows.  The loads go to registers first
+  // (load_tile) and are written to LDS a tile later (commit_tile), so no LDS read ever waits on
+  // a load in flight.
+  uint4 stg[4];
   float strow = 0.0f;
   auto load_tile = [&](int entry) {
     const uint32_t tile_base = (uint32_t)(entry >> 1) * C::BM * C::ROW_BYTES;
+    const buf_rsrc src = wv < 4 ? qbuf : dobuf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = 4 * (4 * w + i) + (lane >> 4);
+      const int row = 4 * ((4 * wv + i) & 15) + (lane >> 4);
       const uint32_t voff = (uint32_t)row * C::ROW_BYTES + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
-      stq[i] = buf_load16(qbuf, voff, tile_base);
-      std_[i] = buf_load16(dobuf, voff, tile_base);
+      stg[i] = buf_load16(src, voff, tile_base);
     }
-    if (w < 2) {
+    if (wv < 2) {
       const uint32_t roff = (uint32_t)(entry >> 1) * C::BM * sizeof(float);
-      strow = __builtin_bit_cast(float, buf_load4(w == 0 ? lbuf : dlbuf, (uint32_t)lane * sizeof(float), roff));
+      strow = __builtin_bit_cast(float, buf_load4(wv == 0 ? lbuf : dlbuf, (uint32_t)lane * sizeof(float), roff));
     }
   };
   auto commit_tile = [&](int b) {
-    unsigned char* qt = bufp(b);
+    unsigned char* t = bufp(b);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 4 * w + i;
-      *reinterpret_cast<uint4*>(qt + j * 1024 + lane * 16) = stq[i];
-      *reinterpret_cast<uint4*>(qt + C::TILE_BYTES + j * 1024 + lane * 16) = std_[i];
-    }
-    if (w < 2) rowsp(b)[w * C::BM + lane] = strow;
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(t + (4 * wv + i) * 1024 + lane * 16) = stg[i];
+    if (wv < 2) rowsp(b)[wv * C::BM + lane] = strow;
   };
 
   // Row mask of this lane's key over a tile's BM query rows starting at q0 (bit i = row q0 + i
-  // masked), pre-shifted by g*KPL so that bit qr*32 + perm_index(r, 0) belongs to register r of
-  // row block qr in this lane group.
+  // masked), pre-shifted by g*KPL so that bit h*32 + perm_index(r, 0) belongs to register r of
+  // unit h in this lane group.
   auto tile_row_mask = [&](int32_t q0) -> uint64_t {
     auto bits = [&](int32_t s0, int32_t e0) -> uint64_t {
       const int32_t lo = s0 <= q0 ? 0 : (s0 >= q0 + 64 ? 64 : s0 - q0);
@@ -200,195 +201,99 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
     return m >> (g * KPL);
   };
 
-  // ---- one 32-query half ("unit") of a tile, in three steps ---------------------------------
-  // S = Q K^T and dP = dO V^T for the tile's rows h*32..h*32+31: register r of group g is query
-  // h*32 + perm_index(r, g); the column is this lane's key.
-  auto sdp = [&](const unsigned char* qt, auto hc, f32x16& sacc, f32x16& pacc) {
-    constexpr int h = decltype(hc)::value;
-    sacc = f32x16{};
-    pacc = f32x16{};
+  // ---- one 32-query unit ----------------------------------------------------------------------
+  // P of unit parity h in LDS: [group][r/4][lane][r%4], so that each 16-byte access of a lane
+  // group is contiguous.
+  auto xoff = [&](int h, int r4) { return ((h * 4 + kg) * 4 + r4) * 64 * 4 + lane * 4; };
+  // Row operands (Q for the P wave, dO for the dS wave) of unit h of the tile at qt.
+  auto read_ops = [&](const unsigned char* qt, int h, frag* op) {
 #pragma unroll
-    for (int st = 0; st < C::QK_STEPS; ++st) {
-      const int off = off_s[st] + h * 32 * C::ROW_BYTES;
-      const frag qa = *reinterpret_cast<const frag*>(qt + off);
-      const frag da = *reinterpret_cast<const frag*>(qt + C::TILE_BYTES + off);
-      sacc = E::mfma(qa, kf[st], sacc);
-      pacc = E::mfma(da, vf[st], pacc);
-    }
+    for (int st = 0; st < C::QK_STEPS; ++st)
+      op[st] = *reinterpret_cast<const frag*>(qt + row_region + off_s[st] + h * 32 * C::ROW_BYTES);
   };
-
-  // P = exp2(S*scale*log2e - LSE2) (0 where masked: bit h*32 + perm_index(r, 0) of mrow) and
-  // dS = P (dP - D), rounded into operand fragments: k-step u covers queries
-  // h*32 + u*KSTEP + g*KPL + e = registers u*KPL + e.
-  struct Rows {
-    float lse[16], dlt[16];  // LSE2 and D of the 16 queries this lane holds
-  };
-  auto load_rows = [&](const float* lse_t, auto hc, Rows& rw) {
+  // op holds this unit's row operands (read one unit ahead); after the barrier the next unit's
+  // are read into it (from qn, half hn) when next is set.
+  auto unit = [&](const unsigned char* qt, auto hc, bool test, uint64_t mrow, auto&& publish,
+                  frag* op, bool next, const unsigned char* qn, int hn) {
     constexpr int h = decltype(hc)::value;
-    const float* dlt_t = lse_t + C::BM;
+    const float* rows = reinterpret_cast<const float*>(qt + 2 * C::TILE_BYTES) + (dsw ? C::BM : 0);
+    // S = Q K^T (P wave) or dP = dO V^T (dS wave): register r of group g is query
+    // h*32 + perm_index(r, g) of the tile; the column is this lane's key.
+    f32x16 sacc = {};
+#pragma unroll
+    for (int st = 0; st < C::QK_STEPS; ++st) sacc = E::mfma(op[st], bop[st], sacc);
+    // LSE2 (P wave) or D (dS wave) of the 16 queries this lane holds: runs of KPL consecutive
+    // rows h*32 + (r/KPL)*2*KPL + g*KPL + 0..KPL-1.
+    float rv[16];
     if constexpr (KPL == 8) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int q = h * 32 + 16 * j + 8 * g;
-        const float4 l0 = *reinterpret_cast<const float4*>(lse_t + q);
-        const float4 l1 = *reinterpret_cast<const float4*>(lse_t + q + 4);
-        const float4 d0 = *reinterpret_cast<const float4*>(dlt_t + q);
-        const float4 d1 = *reinterpret_cast<const float4*>(dlt_t + q + 4);
-        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          rw.lse[8 * j + e] = lv[e];
-          rw.dlt[8 * j + e] = dv[e];
-        }
+        const float4 x0 = *reinterpret_cast<const float4*>(rows + h * 32 + 16 * j + 8 * g);
+        const float4 x1 = *reinterpret_cast<const float4*>(rows + h * 32 + 16 * j + 8 * g + 4);
+        rv[8 * j + 0] = x0.x; rv[8 * j + 1] = x0.y; rv[8 * j + 2] = x0.z; rv[8 * j + 3] = x0.w;
+        rv[8 * j + 4] = x1.x; rv[8 * j + 5] = x1.y; rv[8 * j + 6] = x1.z; rv[8 * j + 7] = x1.w;
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        rw.lse[r] = lse_t[h * 32 + perm_index<KPL>(r, g)];
-        rw.dlt[r] = dlt_t[h * 32 + perm_index<KPL>(r, g)];
+      for (int r = 0; r < 16; ++r) rv[r] = rows[h * 32 + perm_index<KPL>(r, g)];
+    }
+    float pv[16];
+    if (!dsw) {
+      // P = exp2(S*scale*log2e - LSE2); in partly masked tiles 0 where masked
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(fmaf(sacc[r], cexp, -rv[r]));
+      if (test) {
+        const uint32_t mw = (uint32_t)(mrow >> (32 * h));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pv[r] = ((mw >> perm_index<KPL>(r, 0)) & 1u) ? 0.0f : pv[r];
+      }
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(xch + xoff(h, r4)) =
+            make_float4(pv[4 * r4], pv[4 * r4 + 1], pv[4 * r4 + 2], pv[4 * r4 + 3]);
+    }
+    publish();  // workgroup barrier: P of this unit (and possibly the next tile) visible
+    if (dsw) {
+      // dS = P (dP - D)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 p = *reinterpret_cast<const float4*>(xch + xoff(h, r4));
+        pv[4 * r4 + 0] = p.x * (sacc[4 * r4 + 0] - rv[4 * r4 + 0]);
+        pv[4 * r4 + 1] = p.y * (sacc[4 * r4 + 1] - rv[4 * r4 + 1]);
+        pv[4 * r4 + 2] = p.z * (sacc[4 * r4 + 2] - rv[4 * r4 + 2]);
+        pv[4 * r4 + 3] = p.w * (sacc[4 * r4 + 3] - rv[4 * r4 + 3]);
       }
     }
-  };
-  // One 32-query unit with a fixed issue order (a wave per SIMD issues in order): the next
-  // unit's S / dP products are interleaved with this unit's elementwise work
-  //   P = exp2(S*scale*log2e - LSE2) (0 where masked), dS = P (dP - D),
-  // then dV^T += dO^T P and dK^T += Q^T dS run with their transpose reads.  sched_barrier fences
-  // pin the order; operand reads run a few products ahead of their use.
-  constexpr int AH = 4;  // operand reads of the S / dP products issued ahead of their use
-  // The first AH operand reads of a unit's S / dP products can be issued by the unit before it
-  // (pre: they are already in opio; pfn: issue the following unit's into opio, from tile q2,
-  // half h2, at the end of this unit).
-  auto unit = [&](const unsigned char* qt, auto hc, auto maskedc, bool test, uint64_t mrow,
-                  const Rows& rw, const f32x16& sc, const f32x16& pc, const unsigned char* qn,
-                  auto hnc, auto nextc, const float* lse_n, Rows& rw_n, f32x16& sn, f32x16& pn,
-                  frag* opio, auto prec, auto pfnc, const unsigned char* q2, auto h2c,
-                  auto barc, auto&& bar) {
-    constexpr int h = decltype(hc)::value, hn = decltype(hnc)::value, h2 = decltype(h2c)::value;
-    constexpr bool MASKED = decltype(maskedc)::value;
-    constexpr bool NEXT = decltype(nextc)::value;
-    constexpr bool PRE = decltype(prec)::value, PFN = decltype(pfnc)::value;
-    constexpr bool BAR = decltype(barc)::value;  // run bar() before the read-ahead at the end
-    constexpr int NS = 2 * C::QK_STEPS;  // S / dP products of a unit
-    constexpr int NDV = 2 * US * C::NDB, AT = 3;  // dV / dK products of a unit, read-ahead
-    // Registers 0..7 feed the first half of the dV / dK products, 8..15 the second half: the
-    // elementwise work of registers 0..RA-1 runs beside the S / dP products, the rest beside the
-    // first half of the dV / dK products.
-    constexpr int RA = 10;
-    if constexpr (NEXT) load_rows(lse_n, hnc, rw_n);
-    auto sread = [&](int i) -> frag {
-      return *reinterpret_cast<const frag*>(qn + ((i & 1) ? C::TILE_BYTES : 0) + off_s[i >> 1] +
-                                            hn * 32 * C::ROW_BYTES);
-    };
-    // dV / dK product j: k-step u = j / (2 NDB), d block (j % (2 NDB)) / 2, dV (even j) or dK
-    auto tread = [&](int j) -> frag {
-      const int u = j / (2 * C::NDB), db = (j % (2 * C::NDB)) >> 1;
-      return tr_operand((j & 1) ? qt : qt + C::TILE_BYTES, off_tq[db], (h * 32 + u * KSTEP) * C::ROW_BYTES);
-    };
-    frag op[NS], top[NDV];
-    if constexpr (NEXT) {
-      sn = f32x16{};
-      pn = f32x16{};
+    // operand fragments of P or dS: k-step u covers queries h*32 + u*KSTEP + g*KPL + e =
+    // registers u*KPL + e
+    frag fr[US];
 #pragma unroll
-      for (int i = 0; i < AH; ++i) op[i] = PRE ? opio[i] : sread(i);
-    }
-    // P = exp2(S*scale*log2e - LSE2) and dS = P (dP - D) for register r.
-    float pv[16], dsv[16];
-    auto elem = [&](int r) {
-      pv[r] = fast_exp2(fmaf(sc[r], cexp, -rw.lse[r]));
-      dsv[r] = pv[r] * (pc[r] - rw.dlt[r]);
-    };
-    // In partly masked tiles P and dS are zeroed where masked (bit perm_index(r, 0) of this
-    // unit's mask word) before they are rounded into operands; other tiles skip this.
-    const uint32_t mw = (uint32_t)(mrow >> (32 * h));
-    auto apply_mask = [&](int r0, int r1) {
-      if constexpr (MASKED) {
-        if (test) {  // uniform across the wave
-#pragma unroll
-          for (int r = r0; r < r1; ++r) {
-            const bool m = (mw >> perm_index<KPL>(r, 0)) & 1u;
-            pv[r] = m ? 0.0f : pv[r];
-            dsv[r] = m ? 0.0f : dsv[r];
-          }
-        }
-      }
-    };
-    // operand fragments: k-step u covers queries h*32 + u*KSTEP + g*KPL + e = registers u*KPL + e
-    frag pf[US], sf[US];
-    auto frags = [&](int u) {
+    for (int u = 0; u < US; ++u) {
       if constexpr (KPL == 1) {
-        pf[u] = pv[u];
-        sf[u] = dsv[u];
+        fr[u] = pv[u];
       } else {
 #pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-          pf[u][e] = E::from_float(pv[u * KPL + e]);
-          sf[u][e] = E::from_float(dsv[u * KPL + e]);
-        }
+        for (int e = 0; e < KPL; ++e) fr[u][e] = E::from_float(pv[u * KPL + e]);
       }
-    };
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if constexpr (NEXT) {
-        if (i & 1)
-          pn = E::mfma(op[i], vf[i >> 1], pn);
-        else
-          sn = E::mfma(op[i], kf[i >> 1], sn);
-        if (i + AH < NS) op[i + AH] = sread(i + AH);
-      }
-#pragma unroll
-      for (int r = i * RA / NS; r < (i + 1) * RA / NS; ++r) elem(r);
-      if (i + AT >= NS) top[i + AT - NS] = tread(i + AT - NS);
-      __builtin_amdgcn_sched_barrier(0);
     }
-    apply_mask(0, 8);
+    if (next) read_ops(qn, hn, op);
+    // dV^T += dO^T P or dK^T += Q^T dS over the unit's queries
 #pragma unroll
-    for (int u = 0; u < US / 2; ++u) frags(u);
-    __builtin_amdgcn_sched_barrier(0);
-    constexpr int HALF = NDV / 2;
+    for (int u = 0; u < US; ++u)
 #pragma unroll
-    for (int j = 0; j < NDV; ++j) {
-      const int u = j / (2 * C::NDB), db = (j % (2 * C::NDB)) >> 1;
-      if (j & 1)
-        dk_acc[db] = E::mfma(top[j], sf[u], dk_acc[db]);
-      else
-        dv_acc[db] = E::mfma(top[j], pf[u], dv_acc[db]);
-      if (j + AT < NDV) top[j + AT] = tread(j + AT);
-      if constexpr (BAR) {
-        if (j == NDV - AH - 1) bar();
-      }
-      if constexpr (PFN) {
-        if (j >= NDV - AH) {
-          const int i = j - (NDV - AH);
-          opio[i] = *reinterpret_cast<const frag*>(q2 + ((i & 1) ? C::TILE_BYTES : 0) + off_s[i >> 1] +
-                                                   h2 * 32 * C::ROW_BYTES);
-        }
-      }
-      if (j < HALF) {
-#pragma unroll
-        for (int r = RA + j * (16 - RA) / HALF; r < RA + (j + 1) * (16 - RA) / HALF; ++r) elem(r);
-        if (j == HALF - 1) {
-          apply_mask(8, 16);
-#pragma unroll
-          for (int u = US / 2; u < US; ++u) frags(u);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int db = 0; db < C::NDB; ++db)
+        acc[db] = E::mfma(tr_operand(qt + tr_region, off_tq[db], (h * 32 + u * KSTEP) * C::ROW_BYTES),
+                          fr[u], acc[db]);
   };
 
-  // ---- software pipeline over units -----------------------------------------------------------
-  // Tile t sits in buffer t % 3.  While the elementwise step of one unit runs, the S / dP
-  // products of the next unit (the second half of the tile, or the first half of the next tile)
-  // are already issued.  Tile t+1 is waited for, with one workgroup barrier, before the second
-  // unit of tile t; that barrier also frees the buffer of tile t-1, which then receives tile t+2.
+  // ---- the walk over the key block's query tiles ---------------------------------------------
+  // Tile t sits in buffer t % 2.  The barrier of a tile's second unit also publishes tile t+1,
+  // committed just before it into the buffer tile t-1 used (every wave has passed the first
+  // unit's barrier of tile t, so none still reads tile t-1); tile t+2 is then loaded.
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
-  f32x16 sn, pn;  // S / dP of the next unit
-  Rows rw, rw_n;  // LSE2 / D of the current and the next unit
-  frag opio[AH];  // operands read ahead for the next unit's S / dP products
-  int entry = 0, cur = 0;
+  int entry = 0;
+  frag op[C::QK_STEPS];
   if (cnt > 0) {
     entry = __builtin_amdgcn_readfirstlane(lst[0]);
     load_tile(entry);
@@ -396,75 +301,43 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdArgs a) {
     commit_tile(0);
     __syncthreads();
     if (cnt > 1) load_tile(__builtin_amdgcn_readfirstlane(lst[1]));
-    load_rows(rowsp(0), H0{}, rw);
-    sdp(bufp(0), H0{}, sn, pn);
-#pragma unroll
-    for (int i = 0; i < AH; ++i)
-      opio[i] = *reinterpret_cast<const frag*>(bufp(0) + ((i & 1) ? C::TILE_BYTES : 0) + off_s[i >> 1] +
-                                               32 * C::ROW_BYTES);
+    read_ops(bufp(0), 0, op);
   }
-  // Tile t sits in buffer t % 3.
-  auto tile_step = [&](const int t, auto has_next_c, auto maskedc) {
-    constexpr bool HAS_NEXT = decltype(has_next_c)::value;
+  for (int t = 0; t < cnt; ++t) {
+    const int b = t & 1;
     const bool test = (entry & 1) || ragged_block;
-    const uint64_t mrow = decltype(maskedc)::value && test ? tile_row_mask((entry >> 1) * C::BM) : 0ull;
-    const unsigned char* qt = bufp(cur);
-    const float* lse_t = rowsp(cur);
-    const int nxt = cur == 2 ? 0 : cur + 1;
-    // first half, with the second half's S / dP
-    f32x16 sc = sn, pc = pn;
-    auto none = [] {};
-    unit(qt, H0{}, maskedc, test, mrow, rw, sc, pc, qt, H1{}, std::true_type{}, lse_t, rw_n, sn, pn,
-         opio, std::true_type{}, std::false_type{}, qt, H0{}, std::false_type{}, none);
-    rw = rw_n;
-    sc = sn;
-    pc = pn;
-    if constexpr (HAS_NEXT) {
-      // second half, with the next tile's first half
-      entry = __builtin_amdgcn_readfirstlane(lst[t + 1]);
-      wait_vmem();        // tile t+1 is in this wave's registers
-      commit_tile(nxt);   // its buffer last held tile t-2
-      __syncthreads();    // tile t+1 complete in LDS
+    const uint64_t mrow = test ? tile_row_mask((entry >> 1) * C::BM) : 0ull;
+    const unsigned char* qt = bufp(b);
+    unit(qt, H0{}, test, mrow, [] { __syncthreads(); }, op, true, qt, 1);
+    const bool more = t + 1 < cnt;
+    unit(qt, H1{}, test, mrow, [&] {
+      if (more) {
+        wait_vmem();       // tile t+1 is in this wave's registers
+        commit_tile(b ^ 1);
+      }
+      __syncthreads();
       if (t + 2 < cnt) load_tile(__builtin_amdgcn_readfirstlane(lst[t + 2]));
-      unit(qt, H1{}, maskedc, test, mrow, rw, sc, pc, bufp(nxt), H0{}, std::true_type{},
-           rowsp(nxt), rw_n, sn, pn, opio, std::false_type{}, std::true_type{}, bufp(nxt), H1{},
-           std::false_type{}, none);
-      rw = rw_n;
-    } else {
-      unit(qt, H1{}, maskedc, test, mrow, rw, sc, pc, qt, H0{}, std::false_type{}, lse_t, rw_n, sn,
-           pn, opio, std::false_type{}, std::false_type{}, qt, H0{}, std::false_type{}, none);
-    }
-    cur = nxt;
-  };
-  // Every tile takes the row test (an unmasked tile's mask word is zero): one code path keeps
-  // the loop free of branches the accumulators would have to merge across.
-  auto step = [&](const int t, auto has_next_c) { tile_step(t, has_next_c, std::true_type{}); };
-  for (int t = 0; t + 1 < cnt; ++t) step(t, std::true_type{});
-  if (cnt > 0) step(cnt - 1, std::false_type{});
+    }, op, more, bufp(b ^ 1), 0);
+    if (more) entry = __builtin_amdgcn_readfirstlane(lst[t + 1]);
+  }
 
   if (key_ok) {
-    T* dkr = static_cast<T*>(a.dk) + ((size_t)bh * a.nk + key) * D;
-    T* dvr = static_cast<T*>(a.dv) + ((size_t)bh * a.nk + key) * D;
+    T* dst = static_cast<T*>(dsw ? a.dk : a.dv) + ((size_t)bh * a.nk + key) * D;
+    const float sc = dsw ? a.scale : 1.0f;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d0 = db * 32 + 8 * i + 4 * g;
         if constexpr (sizeof(T) == 2) {
-          uint2 ok, ov;
-          ok.x = pack_bf16x2(dk_acc[db][4 * i + 0] * a.scale, dk_acc[db][4 * i + 1] * a.scale);
-          ok.y = pack_bf16x2(dk_acc[db][4 * i + 2] * a.scale, dk_acc[db][4 * i + 3] * a.scale);
-          ov.x = pack_bf16x2(dv_acc[db][4 * i + 0], dv_acc[db][4 * i + 1]);
-          ov.y = pack_bf16x2(dv_acc[db][4 * i + 2], dv_acc[db][4 * i + 3]);
-          *reinterpret_cast<uint2*>(dkr + d0) = ok;
-          *reinterpret_cast<uint2*>(dvr + d0) = ov;
+          uint2 out;
+          out.x = pack_bf16x2(acc[db][4 * i + 0] * sc, acc[db][4 * i + 1] * sc);
+          out.y = pack_bf16x2(acc[db][4 * i + 2] * sc, acc[db][4 * i + 3] * sc);
+          *reinterpret_cast<uint2*>(dst + d0) = out;
         } else {
-          *reinterpret_cast<float4*>(dkr + d0) =
-              make_float4(dk_acc[db][4 * i + 0] * a.scale, dk_acc[db][4 * i + 1] * a.scale,
-                          dk_acc[db][4 * i + 2] * a.scale, dk_acc[db][4 * i + 3] * a.scale);
-          *reinterpret_cast<float4*>(dvr + d0) =
-              make_float4(dv_acc[db][4 * i + 0], dv_acc[db][4 * i + 1], dv_acc[db][4 * i + 2],
-                          dv_acc[db][4 * i + 3]);
+          *reinterpret_cast<float4*>(dst + d0) =
+              make_float4(acc[db][4 * i + 0] * sc, acc[db][4 * i + 1] * sc, acc[db][4 * i + 2] * sc,
+                          acc[db][4 * i + 3] * sc);
         }
       }
   }
@@ -511,7 +384,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin) {
   if (err != hipSuccess) return err;
 
   using C = BwdTile<T, D>;
-  const size_t smem = 3 * (2 * C::TILE_BYTES + 2 * C::BM * sizeof(float));
+  const size_t smem = C::SMEM;
   // The main kernel uses more than 64 KiB of LDS; allow it on the current device.
   err = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_kernel<T, D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -519,7 +392,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin) {
   const int64_t n_kb = (a.nk + C::BN - 1) / C::BN;
   const int64_t grid = n_kb * a.B * a.H;
   if (ev_begin) (void)hipEventRecord(ev_begin, stream);
-  hipLaunchKernelGGL((attn_bwd_kernel<T, D>), dim3((unsigned)grid), dim3(256), smem, stream, a);
+  hipLaunchKernelGGL((attn_bwd_kernel<T, D>), dim3((unsigned)grid), dim3(C::NT), smem, stream, a);
   return hipGetLastError();
 }
 
