@@ -73,8 +73,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int n_qb = (a.nq + C::BM - 1) / C::BM;
   const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
   const int bh = work / n_qb;
-  // Query blocks are visited last-first: under causal-like masks the later blocks have the
-  // longest lists, so the longest work is dispatched first.
+  // Query blocks in the order of a.order (longest lists first, neighbours kept together).
   const int qb = a.order[work % n_qb];
 
   const T* __restrict__ Qp = static_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
