@@ -39,7 +39,8 @@ extern "C" {
 typedef enum {
   FM_OK = 0,
   FM_ERR_NULL = 1,        /* a required pointer is NULL                                      */
-  FM_ERR_SHAPE = 2,       /* a size is out of range (B, H, nq, nk < 1, nq or nk > 2^22, ...) */
+  FM_ERR_SHAPE = 2,       /* a size is out of range (B, H, nq, nk < 1, nq or nk > 2^22, a tile
+                             grid of 2^31 tiles or more, ...) */
   FM_ERR_DTYPE = 3,       /* unknown dtype code                                               */
   FM_ERR_UNSUPPORTED = 4, /* (dtype, d) pair not built                                        */
   FM_ERR_ALIGN = 5,       /* tensor pointer not 16-byte aligned, or vector not 4-byte aligned */
@@ -80,8 +81,11 @@ int32_t flashmask_tile_sizes(int32_t dtype, int32_t d, int32_t* BM_fwd, int32_t*
  * A row with every key masked gets O_i = 0 and LSE_i = -inf.
  * scale: finite and > 0 (else FM_ERR_VALUE).
  * Q [B,H,nq,d], K/V [B,H,nk,d] in `dtype`; O [B,H,nq,d] in `dtype`; LSE float32 [B,H,nq].
+ * Sizes: 1 <= nq, nk <= 2^22, and the tile grid ceil(nq/BM) x ceil(nk/BN) at both tile shapes
+ * (flashmask_tile_sizes) below 2^31 tiles, so nq = nk = 2^22 - 128 is the longest square case.
  * ws: device workspace of at least flashmask_fwd_workspace_bytes(shape) bytes (256-byte
- * aligned), clobbered by the call.
+ * aligned), clobbered by the call; it holds a dense [n_qb][n_kb] list array (8.6 GB at the
+ * longest case, 8 MiB at nq = nk = 131072).
  */
 size_t flashmask_fwd_workspace_bytes(const fm_shape* shape);
 int32_t flashmask_fwd(const fm_shape* shape, const void* Q, const void* K, const void* V,
