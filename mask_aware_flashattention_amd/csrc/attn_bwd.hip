@@ -81,6 +81,18 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   const int kb = a.order[work % n_kb];
   const int key = kb * C::BN + kg * 32 + l32;  // this lane's key (a column of S)
   const bool key_ok = key < a.nk;
+  const int cnt = a.kcnt[kb];
+  if (cnt == 0) {
+    // No listed tile: every query row is masked for these keys, so dK = dV = 0.  Each lane
+    // clears half of its key's row (128 bytes) in the tensor of its wave's role.
+    if (key_ok) {
+      T* row = static_cast<T*>(wv >= 4 ? a.dk : a.dv) + ((size_t)bh * a.nk + key) * D;
+      uint4* p = reinterpret_cast<uint4*>(row + g * (D / 2));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
+  }
 
   const T* __restrict__ Qp = static_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
   const T* __restrict__ dOp = static_cast<const T*>(a.dout) + (size_t)bh * a.nq * D;
@@ -153,7 +165,6 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
 
-  const int cnt = a.kcnt[kb];
   const int32_t* __restrict__ lst = a.klist + (size_t)kb * a.list_stride;
   const float cexp = a.scale * kLog2e;
 

@@ -84,6 +84,17 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   const int q0w = qb * C::BM + w * 32;  // first query row of this wave
   const int q_row = q0w + l32;          // this lane's query row
   const bool row_ok = q_row < a.nq;
+  const int cnt = a.qcnt[qb];
+  if (cnt == 0) {
+    // No listed tile: the block's rows are fully masked, so dQ = 0 (each lane clears half of
+    // its row, 128 bytes).
+    if (row_ok) {
+      uint4* p = reinterpret_cast<uint4*>(static_cast<T*>(a.dq) + ((size_t)bh * a.nq + q_row) * D + g * (D / 2));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
+  }
 
   // Q and dO rows of this lane's query as B operands (k-step s: d = s*KSTEP + g*KPL + 0..KPL);
   // rows past nq read as zeros.
@@ -103,7 +114,6 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   const float lse2 = row_ok ? a.lse2[(size_t)bh * a.nq + q_row] : INFINITY;
   const float dlt = row_ok ? a.delta[(size_t)bh * a.nq + q_row] : 0.0f;
 
-  const int cnt = a.qcnt[qb];
   const int32_t* __restrict__ lst = a.qlist + (size_t)qb * a.list_stride;
   const int last_kb = (a.nk - 1) / C::BN;
   const bool ragged = (a.nk % C::BN) != 0;

@@ -86,6 +86,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int q0w = qb * C::BM + w * 32;  // first query row of this wave
   const int q_row = q0w + l32;          // this lane's query row
   const bool row_ok = q_row < a.nq;
+  const int cnt = a.qcnt[qb];
+  if (cnt == 0) {
+    // No listed tile: the block's rows are fully masked: O = 0, LSE = -inf (each lane clears
+    // half of its row, 128 bytes).
+    if (row_ok) {
+      uint4* p = reinterpret_cast<uint4*>(static_cast<T*>(a.o) + ((size_t)bh * a.nq + q_row) * D + g * (D / 2));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (g == 0) a.lse[(size_t)bh * a.nq + q_row] = -INFINITY;
+    }
+    return;
+  }
 
   // Q^T as the B operand of S^T = K Q^T: k-step s holds Q[q_row][s*KSTEP + g*KPL + 0..KPL).
   frag qf[C::QK_STEPS];
@@ -99,7 +111,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     }
   }
 
-  const int cnt = a.qcnt[qb];
   const int32_t* __restrict__ lst = a.qlist + (size_t)qb * a.list_stride;
   const int last_kb = (a.nk - 1) / C::BN;
   const bool ragged = (a.nk % C::BN) != 0;
