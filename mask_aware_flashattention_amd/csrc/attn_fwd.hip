@@ -34,25 +34,16 @@ template <typename T, int D>
 struct FwdTile {
   static constexpr int BM = 128, BN = 64, NT = 256;
   static constexpr int KPL = Elem<T>::KPL, KSTEP = 2 * KPL;
-  static constexpr int CH = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  static constexpr int CPR = D / CH;              // 16-byte chunks per K/V row
-  static constexpr int K_LD = D + CH;             // padded K row (elements)
+  static constexpr int ROW_BYTES = D * (int)sizeof(T);
   static constexpr int NRB = BN / 32;             // 32-key row blocks of S^T
   static constexpr int NDB = D / 32;              // 32-wide d blocks of O^T
-  static constexpr int QK_STEPS = D / KSTEP;
-  static constexpr int PV_STEPS = BN / KSTEP;
-  static constexpr int ROW_BYTES = D * (int)sizeof(T);
-  static_assert(CPR == 16, "thread mapping assumes 256-byte rows");
-  static_assert(BN == 4 * (NT / CPR), "staging: 4 rows per thread");
+  static constexpr int QK_STEPS = D / KSTEP;      // k-steps of the score product
+  static constexpr int PV_STEPS = BN / KSTEP;     // k-steps of the P V product
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;
+  static constexpr int MW_BYTES = 4 * BN * 4;     // per wave, per key: one 32-bit row mask
+  static_assert(ROW_BYTES == 256, "256-byte rows");
+  static_assert(TILE_BYTES == 16 * 1024, "16 blocks of 1 KiB per tile");
 };
-
-// 16-byte chunk c of V row `key` lives at chunk c ^ vswz(key): consecutive keys land in
-// different bank groups, which keeps the transpose reads (4 keys x 4 chunks per 32 lanes)
-// conflict-free on the 64-bank LDS.
-template <typename T>
-__device__ __host__ constexpr int vswz(int key) {
-  return sizeof(T) == 2 ? 4 * (key & 3) : 0;
-}
 
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
@@ -61,14 +52,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   using C = FwdTile<T, D>;
   using E = Elem<T>;
   using frag = typename E::frag;
-  constexpr int KPL = C::KPL, KSTEP = C::KSTEP, CH = C::CH;
+  constexpr int KPL = C::KPL, KSTEP = C::KSTEP;
 
-  __shared__ __attribute__((aligned(16))) T k_lds[C::BN * C::K_LD];
-  __shared__ __attribute__((aligned(16))) T v_lds[C::BN * D];
-  __shared__ __attribute__((aligned(16))) uint32_t mw_lds[4][C::BN];  // per wave, per key
+  // LDS: two buffers [K | V | mask words].  They are separate arrays so that the compiler can
+  // tell that loads into one buffer never overlap reads of the other, and adds no wait on the
+  // loads in flight before those reads.
+  constexpr int BUF_BYTES = 2 * C::TILE_BYTES + C::MW_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[BUF_BYTES];
+  auto bufp = [&](auto bc) -> unsigned char* {
+    if constexpr (decltype(bc)::value == 0)
+      return lds0;
+    else
+      return lds1;
+  };
+  auto mwp = [&](auto bc) -> uint32_t* {
+    return reinterpret_cast<uint32_t*>(bufp(bc) + 2 * C::TILE_BYTES);
+  };
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int n_qb = (a.nq + C::BM - 1) / C::BM;
   const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
@@ -99,7 +103,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     return;
   }
 
-  // Q^T as the B operand of S^T = K Q^T: k-step s holds Q[q_row][s*KSTEP + g*KPL + 0..KPL).
+  // Q^T as the B operand of S^T = K Q^T: k-step s holds Q[q_row][s*KSTEP + g*KPL + 0..KPL);
+  // rows past nq read as zeros.
   frag qf[C::QK_STEPS];
 #pragma unroll
   for (int s = 0; s < C::QK_STEPS; ++s) {
@@ -114,100 +119,109 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const int32_t* __restrict__ lst = a.qlist + (size_t)qb * a.list_stride;
   const int last_kb = (a.nk - 1) / C::BN;
   const bool ragged = (a.nk % C::BN) != 0;
+  const float cexp = a.scale * kLog2e;
 
-  // staging map: chunk c of a 256-byte row; K rows r0 + 16*i, V rows r0 + 16*i
-  const int c = tid % C::CPR;
-  const int r0 = tid / C::CPR;
-  const uint32_t lane_off = (uint32_t)r0 * C::ROW_BYTES + (uint32_t)c * 16;
-  const int mkey = tid & 63;  // mask word: key mkey of the tile, for wave w's 32 rows
-  uint4 kreg[4], vreg[4];
-  uint32_t mword = 0;
+  // Per-lane LDS byte offsets; the swizzle depends on row & 15 only, so row blocks of 16 keys
+  // share them.  K operand of S^T: the permuted row source of lane l32, k-step s.  V^T operand:
+  // transpose-read rows (tr_row, tr_row + 4) and columns 32*db + tr_col of a 16-key step (fp32:
+  // row g, column 32*db + l32 of a 2-key step).
+  int off_k[C::QK_STEPS];
+  int off_v[C::NDB][2];
+  {
+    const int srow = row_source<KPL>(l32);
+#pragma unroll
+    for (int s = 0; s < C::QK_STEPS; ++s)
+      off_k[s] = tile_off<T, 0>(srow, s * KSTEP + g * KPL, C::ROW_BYTES);
+    const int tb = lane >> 4, ti = lane & 15;
+    const int tr_row = 8 * (tb >> 1) + (ti >> 2);
+    const int tr_col = 16 * (tb & 1) + 4 * (ti & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+        off_v[db][h] = KPL == 8 ? tile_off<T, 0>(tr_row + 4 * h, 32 * db + tr_col, C::ROW_BYTES)
+                                : tile_off<T, 0>(g, 32 * db + l32, C::ROW_BYTES);
+  }
 
-  auto load_tile = [&](int entry) {
+  // Stage key tile `entry` into buffer `bufc`: K then V, 16 blocks of 1 KiB each, wave w fills
+  // blocks 4w..4w+3 (lane l: row 4j + l/16, physical chunk l%16 = logical chunk
+  // (l%16) ^ swz_row(row)); keys past nk read as zeros.  In partly masked tiles lane l also
+  // writes the row mask of key l for this wave's 32 rows; the four vector loads go out before
+  // the tile's loads, so that waiting for them does not wait for the tile.
+  auto issue_tile = [&](int entry, auto bufc) {
     const int kb = entry >> 1;
-    const uint32_t tile_off = (uint32_t)kb * C::BN * C::ROW_BYTES;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kreg[i] = buf_load16(kbuf, lane_off + i * 16 * C::ROW_BYTES, tile_off);
-      vreg[i] = buf_load16(vbuf, lane_off + i * 16 * C::ROW_BYTES, tile_off);
-    }
     const bool test = (entry & 1) || (kb == last_kb && ragged);
-    if (test) {
-      const int j = kb * C::BN + mkey;
-      if (j < a.nk) {
-        // rows [q0w, q0w + 32) of this wave inside [s, e): bits [lo, hi)
-        auto bits = [&](int32_t s, int32_t e) -> uint32_t {
-          const int32_t lo = s <= q0w ? 0 : (s >= q0w + 32 ? 32 : s - q0w);
-          const int32_t hi = e <= q0w ? 0 : (e >= q0w + 32 ? 32 : e - q0w);
-          if (hi <= lo) return 0u;
-          const uint32_t upto_hi = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
-          const uint32_t upto_lo = (1u << lo) - 1u;  // lo < 32 here
-          return upto_hi & ~upto_lo;
-        };
-        mword = bits(a.mask.lts[j], a.mask.lte[j]) | bits(a.mask.uts[j], a.mask.ute[j]);
-      } else {
-        mword = 0xffffffffu;  // past the last key: masked for every row
-      }
+    const int jk = kb * C::BN + lane;
+    const bool live = jk < a.nk;  // keys past nk are masked for every row
+    int32_t s0 = 0, e0 = 0, s1 = 0, e1 = 0;
+    if (test && live) {
+      s0 = a.mask.lts[jk];
+      e0 = a.mask.lte[jk];
+      s1 = a.mask.uts[jk];
+      e1 = a.mask.ute[jk];
     }
-  };
-
-  auto store_tile = [&](bool test) {
+    unsigned char* kt = bufp(bufc);
+    const uint32_t tile_base = (uint32_t)kb * C::BN * C::ROW_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = r0 + 16 * i;
-      *reinterpret_cast<uint4*>(&k_lds[row * C::K_LD + c * CH]) = kreg[i];
-      *reinterpret_cast<uint4*>(&v_lds[row * D + (c ^ vswz<T>(row)) * CH]) = vreg[i];
+      const int j = 4 * w + i;
+      const int row = 4 * j + (lane >> 4);
+      const uint32_t voff = (uint32_t)row * C::ROW_BYTES + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
+      buf_load_lds<16>(kbuf, kt + j * 1024, voff, tile_base);
+      buf_load_lds<16>(vbuf, kt + C::TILE_BYTES + j * 1024, voff, tile_base);
     }
-    if (test) mw_lds[w][mkey] = mword;
+    if (test) {
+      // rows [q0w, q0w + 32) inside [s, e): bits [lo, hi)
+      auto bits = [&](int32_t s, int32_t e) -> uint32_t {
+        const int32_t lo = s <= q0w ? 0 : (s >= q0w + 32 ? 32 : s - q0w);
+        const int32_t hi = e <= q0w ? 0 : (e >= q0w + 32 ? 32 : e - q0w);
+        if (hi <= lo) return 0u;
+        const uint32_t upto_hi = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
+        return upto_hi & ~((1u << lo) - 1u);  // lo < 32 here
+      };
+      mwp(bufc)[w * C::BN + lane] = live ? (bits(s0, e0) | bits(s1, e1)) : 0xffffffffu;
+    }
   };
 
   f32x16 oacc[C::NDB];
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+  for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;  // reference max (scale*log2(e) units) for this lane's row
   float l_run = 0.0f;       // this lane's share of the running sum (its 32 keys of each tile)
-  const float cexp = a.scale * kLog2e;
 
-  // transpose-read address of the V^T operand (bf16): lane i of 16-lane block b reads
-  // V[k0 + i/4][m0 + 4*(i%4)] with m0 = 16*(b%2) + 32*db, k0 = t*KSTEP + 8*(b/2) (+4).
-  const int tb = lane >> 4, ti = lane & 15;
-  const int tr_krow = 8 * (tb >> 1) + (ti >> 2);  // + t*KSTEP (+4)
-  const int tr_col = 16 * (tb & 1) + 4 * (ti & 3);  // + 32*db (elements)
+  int entry = __builtin_amdgcn_readfirstlane(lst[0]);
 
-  // List entries are read into scalar registers (the buffer loads take the tile offset as a
-  // scalar operand).
-  if (cnt > 0) load_tile(__builtin_amdgcn_readfirstlane(lst[0]));
-
-  for (int it = 0; it < cnt; ++it) {
-    const int entry = __builtin_amdgcn_readfirstlane(lst[it]);
+  auto body = [&](const int it, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int kb = entry >> 1;
     const bool test = (entry & 1) || (kb == last_kb && ragged);
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile(test);
-    __syncthreads();
-    if (it + 1 < cnt) load_tile(__builtin_amdgcn_readfirstlane(lst[it + 1]));
+    const int next = it + 1 < cnt ? __builtin_amdgcn_readfirstlane(lst[it + 1]) : 0;
+    wait_vmem();      // this wave's loads of tile `it` have landed in LDS
+    __syncthreads();  // ... everyone's, and the mask words; the other buffer is free
+    if (it + 1 < cnt) issue_tile(next, std::integral_constant<int, buf ^ 1>{});
 
-    // S^T = K Q^T: accumulator register r of group g in row block rb is key
-    // rb*32 + perm_index(r, g) of the tile, column = this lane's query.
+    const unsigned char* kt = bufp(bufc);
+    const unsigned char* vt = kt + C::TILE_BYTES;
+
+    // S^T = K Q^T: register r of group g in row block rb is tile key rb*32 + perm_index(r, g);
+    // the column is this lane's query.
     f32x16 sacc[C::NRB];
 #pragma unroll
     for (int rb = 0; rb < C::NRB; ++rb) {
-      const T* kp = &k_lds[(rb * 32 + row_source<KPL>(l32)) * C::K_LD + g * KPL];
-      sacc[rb] = E::mfma(E::load_frag(kp), qf[0], f32x16{});
+      sacc[rb] = f32x16{};
 #pragma unroll
-      for (int s = 1; s < C::QK_STEPS; ++s)
-        sacc[rb] = E::mfma(E::load_frag(kp + s * KSTEP), qf[s], sacc[rb]);
+      for (int st = 0; st < C::QK_STEPS; ++st)
+        sacc[rb] = E::mfma(*reinterpret_cast<const frag*>(kt + off_k[st] + rb * 32 * C::ROW_BYTES),
+                           qf[st], sacc[rb]);
     }
 
     if (test) {
-      // keys rb*32 + (r/KPL)*2*KPL + g*KPL + r%KPL: runs of KPL consecutive keys
+      const uint32_t* mw = mwp(bufc) + w * C::BN;
 #pragma unroll
       for (int rb = 0; rb < C::NRB; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t word = mw_lds[w][rb * 32 + perm_index<KPL>(r, g)];
+          const uint32_t word = mw[rb * 32 + perm_index<KPL>(r, g)];
           sacc[rb][r] = ((word >> l32) & 1u) ? -INFINITY : sacc[rb][r];
         }
     }
@@ -233,8 +247,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     }
     const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 
-    // P^T (exp2 of the scaled scores) as operand fragments; the row sum stays in fp32 (a sum of
-    // bf16-rounded values would cost up to 2^-9 relative on short rows, too much for the LSE).
+    // P^T (exp2 of the scaled scores) as operand fragments: k-step t covers tile keys
+    // t*KSTEP + g*KPL + e = registers (t*KPL)%16 + e of row block (t*KPL)/16.  The row sum stays
+    // in fp32 (a sum of bf16-rounded values would cost up to 2^-9 relative on short rows, too
+    // much for the LSE).
     frag pf[C::PV_STEPS];
 #pragma unroll
     for (int t = 0; t < C::PV_STEPS; ++t) {
@@ -251,27 +267,35 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       }
     }
 
-    // O^T += V^T P^T.  k-step t covers tile keys t*KSTEP + g*KPL + e.
+    // O^T += V^T P^T (contraction over the tile's keys; V^T read with the transpose read).
 #pragma unroll
     for (int t = 0; t < C::PV_STEPS; ++t) {
+      const int k0_bytes = t * KSTEP * C::ROW_BYTES;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
         frag vf;
         if constexpr (KPL == 8) {
-          const int k0 = t * KSTEP + tr_krow;
-          const int col = 32 * db + tr_col;
-          const int ch = col / 8, half = (col % 8) / 4;
-          const T* p0 = &v_lds[k0 * D + ((ch ^ vswz<T>(k0)) * CH) + half * 4];
-          const T* p1 = &v_lds[(k0 + 4) * D + ((ch ^ vswz<T>(k0 + 4)) * CH) + half * 4];
-          const s16x4 lo = lds_read_tr16(p0), hi = lds_read_tr16(p1);
+          const s16x4 lo = lds_read_tr16(vt + off_v[db][0] + k0_bytes);
+          const s16x4 hi = lds_read_tr16(vt + off_v[db][1] + k0_bytes);
           vf = __builtin_bit_cast(frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
-          vf = v_lds[(t * KSTEP + g) * D + 32 * db + l32];
+          vf = *reinterpret_cast<const T*>(vt + off_v[db][0] + k0_bytes);
         }
         oacc[db] = E::mfma(vf, pf[t], oacc[db]);
       }
     }
+    entry = next;
+  };
+
+  issue_tile(entry, std::integral_constant<int, 0>{});
+  // Unrolled by two so each buffer index is a compile-time constant; an odd last tile runs after
+  // the loop, so the loop body has no conditional path the accumulators must merge across.
+  int it = 0;
+  for (; it + 1 < cnt; it += 2) {
+    body(it, std::integral_constant<int, 0>{});
+    body(it + 1, std::integral_constant<int, 1>{});
   }
+  if (it < cnt) body(it, std::integral_constant<int, 0>{});
 
   const float l = l_run + wave_xor32(l_run);
   if (row_ok) {

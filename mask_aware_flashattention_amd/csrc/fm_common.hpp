@@ -78,6 +78,26 @@ __device__ __host__ constexpr int row_source(int m) {
 
 __device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32); }
 
+// Empty asm that takes a value in vector registers: the value must be computed before this
+// point, so code placement passes cannot move its computation into later blocks.
+template <typename X>
+__device__ inline void pin_value(X& x) {
+  static_assert(sizeof(X) % 4 == 0 && sizeof(X) <= 16, "1 to 4 registers");
+  if constexpr (sizeof(X) == 16) {
+    u32x4 u = __builtin_bit_cast(u32x4, x);
+    asm volatile("" : "+v"(u));
+    x = __builtin_bit_cast(X, u);
+  } else if constexpr (sizeof(X) == 8) {
+    u32x2 u = __builtin_bit_cast(u32x2, x);
+    asm volatile("" : "+v"(u));
+    x = __builtin_bit_cast(X, u);
+  } else {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    asm volatile("" : "+v"(u));
+    x = __builtin_bit_cast(X, u);
+  }
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Round float to bf16 (round to nearest even) and pack two into a 32-bit word.
