@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     for (int rb = 0; rb < C::NRB; ++rb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][r]);
-    mx = fmaxf(mx, wave_xor32(mx)) * cexp;
+    mx = pair_max32(mx) * cexp;
     // Move the reference max only when it grows by more than the threshold: probabilities
     // then stay below 2^threshold and the O rescale (a pass over 64 registers) is rare.
     const bool grow = mx > m_run + kRescaleThreshold;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   }
   if (it < cnt) body(it, std::integral_constant<int, 0>{});
 
-  const float l = l_run + wave_xor32(l_run);
+  const float l = pair_sum32(l_run);
   if (row_ok) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     if (g == 0)

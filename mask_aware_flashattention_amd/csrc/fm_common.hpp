@@ -76,7 +76,27 @@ __device__ __host__ constexpr int row_source(int m) {
   return perm_index<KPL>(4 * (m / 8) + (m % 4), (m / 4) % 2);
 }
 
-__device__ inline float wave_xor32(float x) { return __shfl_xor(x, 32); }
+// The two 32-lane halves of x, each across the whole wave: lo[l] = x[l % 32] and
+// hi[l] = x[l % 32 + 32].  v_permlane32_swap exchanges lanes 32..63 of its first operand with
+// lanes 0..31 of its second, in registers (no LDS round trip); the s_nop pairs cover the
+// wait states around a cross-lane VALU operation.
+__device__ inline void wave_halves(float x, float& lo, float& hi) {
+  float a = x, b = x;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  lo = a;
+  hi = b;
+}
+// max / sum of x over lanes l and l ^ 32, the same value in both lanes.
+__device__ inline float pair_max32(float x) {
+  float lo, hi;
+  wave_halves(x, lo, hi);
+  return fmaxf(lo, hi);
+}
+__device__ inline float pair_sum32(float x) {
+  float lo, hi;
+  wave_halves(x, lo, hi);
+  return lo + hi;
+}
 
 // Empty asm that takes a value in vector registers: the value must be computed before this
 // point, so code placement passes cannot move its computation into later blocks.
