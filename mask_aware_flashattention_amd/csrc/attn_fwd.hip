@@ -145,43 +145,49 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 
   // Stage key tile `entry` into buffer `bufc`: K then V, 16 blocks of 1 KiB each, wave w fills
   // blocks 4w..4w+3 (lane l: row 4j + l/16, physical chunk l%16 = logical chunk
-  // (l%16) ^ swz_row(row)); keys past nk read as zeros.  In partly masked tiles lane l also
-  // writes the row mask of key l for this wave's 32 rows; the four vector loads go out before
-  // the tile's loads, so that waiting for them does not wait for the tile.
-  auto issue_tile = [&](int entry, auto bufc) {
-    const int kb = entry >> 1;
-    const bool test = (entry & 1) || (kb == last_kb && ragged);
-    const int jk = kb * C::BN + lane;
-    const bool live = jk < a.nk;  // keys past nk are masked for every row
-    int32_t s0 = 0, e0 = 0, s1 = 0, e1 = 0;
-    if (test && live) {
-      s0 = a.mask.lts[jk];
-      e0 = a.mask.lte[jk];
-      s1 = a.mask.uts[jk];
-      e1 = a.mask.ute[jk];
-    }
+  // (l%16) ^ swz_row(row)); keys past nk read as zeros.  Part i is one K and one V block; the
+  // parts are spread over the score products, because eight waves issuing their loads at once
+  // stall in order on the full memory queue before any of them reaches its products.
+  auto stage_part = [&](int entry, auto bufc, int i) {
     unsigned char* kt = bufp(bufc);
-    const uint32_t tile_base = (uint32_t)kb * C::BN * C::ROW_BYTES;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 4 * w + i;
-      const int row = 4 * j + (lane >> 4);
-      const uint32_t voff = (uint32_t)row * C::ROW_BYTES + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
-      buf_load_lds<16>(kbuf, kt + j * 1024, voff, tile_base);
-      buf_load_lds<16>(vbuf, kt + C::TILE_BYTES + j * 1024, voff, tile_base);
-    }
-    if (test) {
-      // rows [q0w, q0w + 32) inside [s, e): bits [lo, hi)
-      auto bits = [&](int32_t s, int32_t e) -> uint32_t {
-        const int32_t lo = s <= q0w ? 0 : (s >= q0w + 32 ? 32 : s - q0w);
-        const int32_t hi = e <= q0w ? 0 : (e >= q0w + 32 ? 32 : e - q0w);
-        if (hi <= lo) return 0u;
-        const uint32_t upto_hi = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
-        return upto_hi & ~((1u << lo) - 1u);  // lo < 32 here
-      };
-      mwp(bufc)[w * C::BN + lane] = live ? (bits(s0, e0) | bits(s1, e1)) : 0xffffffffu;
-    }
+    const uint32_t tile_base = (uint32_t)(entry >> 1) * C::BN * C::ROW_BYTES;
+    const int j = 4 * w + i;
+    const int row = 4 * j + (lane >> 4);
+    const uint32_t voff = (uint32_t)row * C::ROW_BYTES + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
+    buf_load_lds<16>(kbuf, kt + j * 1024, voff, tile_base);
+    buf_load_lds<16>(vbuf, kt + C::TILE_BYTES + j * 1024, voff, tile_base);
   };
+  // Row mask of a partly masked tile: lane l loads the four vectors at key l of the tile early
+  // and writes the word for this wave's 32 rows (bit t = row q0w + t masked) late, so the wait
+  // for the vectors does not hold up the products in between.
+  struct MaskKey {
+    int32_t s0, e0, s1, e1;
+    bool live;
+  };
+  auto mask_load = [&](int entry) {
+    MaskKey m{0, 0, 0, 0, false};
+    const int jk = (entry >> 1) * C::BN + lane;
+    m.live = jk < a.nk;  // keys past nk are masked for every row
+    if (m.live) {
+      m.s0 = a.mask.lts[jk];
+      m.e0 = a.mask.lte[jk];
+      m.s1 = a.mask.uts[jk];
+      m.e1 = a.mask.ute[jk];
+    }
+    return m;
+  };
+  auto mask_store = [&](const MaskKey& m, auto bufc) {
+    // rows [q0w, q0w + 32) inside [s, e): bits [lo, hi)
+    auto bits = [&](int32_t s, int32_t e) -> uint32_t {
+      const int32_t lo = s <= q0w ? 0 : (s >= q0w + 32 ? 32 : s - q0w);
+      const int32_t hi = e <= q0w ? 0 : (e >= q0w + 32 ? 32 : e - q0w);
+      if (hi <= lo) return 0u;
+      const uint32_t upto_hi = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
+      return upto_hi & ~((1u << lo) - 1u);  // lo < 32 here
+    };
+    mwp(bufc)[w * C::BN + lane] = m.live ? (bits(m.s0, m.e0) | bits(m.s1, m.e1)) : 0xffffffffu;
+  };
+  auto is_test = [&](int entry) { return (entry & 1) || ((entry >> 1) == last_kb && ragged); };
 
   f32x16 oacc[C::NDB];
 #pragma unroll
@@ -193,12 +199,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 
   auto body = [&](const int it, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    const int kb = entry >> 1;
-    const bool test = (entry & 1) || (kb == last_kb && ragged);
-    const int next = it + 1 < cnt ? __builtin_amdgcn_readfirstlane(lst[it + 1]) : 0;
+    const auto other = std::integral_constant<int, buf ^ 1>{};
+    const bool test = is_test(entry);
+    // The last tile stages its own rows again into the free buffer, which is never read: the
+    // staging then needs no branch inside the products.
+    const bool has_next = it + 1 < cnt;
+    const int next = has_next ? __builtin_amdgcn_readfirstlane(lst[it + 1]) : entry;
+    const bool next_test = has_next && is_test(next);
     wait_vmem();      // this wave's loads of tile `it` have landed in LDS
     __syncthreads();  // ... everyone's, and the mask words; the other buffer is free
-    if (it + 1 < cnt) issue_tile(next, std::integral_constant<int, buf ^ 1>{});
+    MaskKey mk{0, 0, 0, 0, false};
+    if (next_test) mk = mask_load(next);
 
     const unsigned char* kt = bufp(bufc);
     const unsigned char* vt = kt + C::TILE_BYTES;
@@ -210,9 +221,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     for (int rb = 0; rb < C::NRB; ++rb) {
       sacc[rb] = f32x16{};
 #pragma unroll
-      for (int st = 0; st < C::QK_STEPS; ++st)
+      for (int st = 0; st < C::QK_STEPS; ++st) {
         sacc[rb] = E::mfma(*reinterpret_cast<const frag*>(kt + off_k[st] + rb * 32 * C::ROW_BYTES),
                            qf[st], sacc[rb]);
+        constexpr int every = C::QK_STEPS * C::NRB / 4;
+        if ((rb * C::QK_STEPS + st) % every == every - 1)
+          stage_part(next, other, (rb * C::QK_STEPS + st) / every);
+      }
     }
 
     if (test) {
@@ -284,10 +299,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
         oacc[db] = E::mfma(vf, pf[t], oacc[db]);
       }
     }
+    if (next_test) mask_store(mk, other);
     entry = next;
   };
 
-  issue_tile(entry, std::integral_constant<int, 0>{});
+  {
+    const auto first = std::integral_constant<int, 0>{};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) stage_part(entry, first, i);
+    if (is_test(entry)) mask_store(mask_load(entry), first);
+  }
   // Unrolled by two so each buffer index is a compile-time constant; an odd last tile runs after
   // the loop, so the loop body has no conditional path the accumulators must merge across.
   int it = 0;
