@@ -15,9 +15,12 @@
 //   * each lane owns one query row (a column of S^T), so the row max and row sum need a single
 //     exchange with the lane 32 apart, and the O^T rescale is a per-lane scalar; the running
 //     max is only moved when a row's max grows by more than 2^8, so rescales are rare;
-//   * K (row-padded) and V (row-major, 16-byte chunks XOR-swizzled by row) are staged in LDS;
-//     the V^T operand is read with the gfx950 LDS transpose read, so V is never transposed in
-//     memory; the next tile's global loads are in flight while the current tile computes;
+//   * K and V tiles go from HBM straight into LDS (buffer loads into LDS, 16-byte chunks
+//     XOR-swizzled by row), double-buffered with one barrier per tile; the next tile's loads are
+//     in flight while the current tile computes; the V^T operand is read with the gfx950 LDS
+//     transpose read, so V is never transposed in memory;
+//   * the row max and the row sum are exchanged between the two lanes of a row with
+//     v_permlane32_swap (registers only);
 //   * in partly masked tiles each wave first turns the four vectors of the tile's keys into one
 //     32-bit word per key (bit t = query row t of the wave is masked), so the per-score test is a
 //     bit extract.
