@@ -222,20 +222,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
     for (int st = 0; st < C::QK_STEPS; ++st)
       op[st] = *reinterpret_cast<const frag*>(qt + row_region + off_s[st] + h * 32 * C::ROW_BYTES);
   };
-  // op holds this unit's row operands (read one unit ahead); after the barrier the next unit's
-  // are read into it (from qn, half hn) when next is set.
-  auto unit = [&](const unsigned char* qt, auto hc, bool test, uint64_t mrow, auto&& publish,
-                  frag* op, bool next, const unsigned char* qn, int hn) {
-    constexpr int h = decltype(hc)::value;
+  // Rows of a unit's LSE2 (P wave) or D (dS wave) for the 16 queries this lane holds: runs of
+  // KPL consecutive rows h*32 + (r/KPL)*2*KPL + g*KPL + 0..KPL-1.
+  auto read_rows = [&](const unsigned char* qt, int h, float* rv) {
     const float* rows = reinterpret_cast<const float*>(qt + 2 * C::TILE_BYTES) + (dsw ? C::BM : 0);
-    // S = Q K^T (P wave) or dP = dO V^T (dS wave): register r of group g is query
-    // h*32 + perm_index(r, g) of the tile; the column is this lane's key.
-    f32x16 sacc = {};
-#pragma unroll
-    for (int st = 0; st < C::QK_STEPS; ++st) sacc = E::mfma(op[st], bop[st], sacc);
-    // LSE2 (P wave) or D (dS wave) of the 16 queries this lane holds: runs of KPL consecutive
-    // rows h*32 + (r/KPL)*2*KPL + g*KPL + 0..KPL-1.
-    float rv[16];
     if constexpr (KPL == 8) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -248,9 +238,53 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) rv[r] = rows[h * 32 + perm_index<KPL>(r, g)];
     }
-    float pv[16];
-    if (!dsw) {
-      // P = exp2(S*scale*log2e - LSE2); in partly masked tiles 0 where masked
+  };
+  // operand fragments of P or dS: k-step u covers queries h*32 + u*KSTEP + g*KPL + e =
+  // registers u*KPL + e
+  auto to_frags = [&](const float* pv, frag* fr) {
+#pragma unroll
+    for (int u = 0; u < US; ++u) {
+      if constexpr (KPL == 1) {
+        fr[u] = pv[u];
+      } else {
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) fr[u][e] = E::from_float(pv[u * KPL + e]);
+      }
+    }
+  };
+  // dV^T += dO^T P or dK^T += Q^T dS over the 32 queries of unit h of the tile at qt.
+  auto accumulate = [&](const unsigned char* qt, int h, const frag* fr) {
+#pragma unroll
+    for (int u = 0; u < US; ++u)
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+        acc[db] = E::mfma(tr_operand(qt + tr_region, off_tq[db], (h * 32 + u * KSTEP) * C::ROW_BYTES),
+                          fr[u], acc[db]);
+  };
+
+  // One step per 32-query unit, one workgroup barrier per step (publish).  The dS wave runs one
+  // unit behind the P wave, so the two waves of a SIMD alternate between matrix and vector work
+  // instead of contending for the matrix core at the same time:
+  //   P wave,  unit (qt, h):  S = Q K^T; P = exp2(S*scale*log2e - LSE2), 0 where masked; P to
+  //                           exchange slot h; barrier; dV^T += dO^T P.
+  //   dS wave:                the pending unit (qp, 1-h), whose P was published at the previous
+  //                           barrier: dS = P (dP - D), dK^T += Q^T dS; then dP = dO V^T of unit
+  //                           (qt, h), kept for the next step; barrier.
+  // op holds the unit's row operands (read one unit ahead); after the barrier the next unit's
+  // are read into it (from qn, half hn) when next is set.
+  auto step = [&](auto role, const unsigned char* qt, auto hc, bool test, uint64_t mrow,
+                  auto&& publish, frag* op, f32x16& dp_prev, bool next, const unsigned char* qn,
+                  int hn, const unsigned char* qp, bool pending) {
+    constexpr int h = decltype(hc)::value;
+    constexpr bool DS = decltype(role)::value;
+    if constexpr (!DS) {
+      // S = Q K^T: register r of group g is query h*32 + perm_index(r, g) of the tile; the
+      // column is this lane's key.
+      f32x16 sacc = {};
+#pragma unroll
+      for (int st = 0; st < C::QK_STEPS; ++st) sacc = E::mfma(op[st], bop[st], sacc);
+      float rv[16], pv[16];
+      read_rows(qt, h, rv);
 #pragma unroll
       for (int r = 0; r < 16; ++r) pv[r] = fast_exp2(fmaf(sacc[r], cexp, -rv[r]));
       if (test) {
@@ -262,74 +296,99 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
       for (int r4 = 0; r4 < 4; ++r4)
         *reinterpret_cast<float4*>(xch + xoff(h, r4)) =
             make_float4(pv[4 * r4], pv[4 * r4 + 1], pv[4 * r4 + 2], pv[4 * r4 + 3]);
-    }
-    publish();  // workgroup barrier: P of this unit (and possibly the next tile) visible
-    if (dsw) {
-      // dS = P (dP - D)
+      publish();  // workgroup barrier: P of this unit (and possibly the next tile) visible
+      frag fr[US];
+      to_frags(pv, fr);
+      if (next) read_ops(qn, hn, op);
+      accumulate(qt, h, fr);
+    } else {
+      if (pending) {
+        // dS = P (dP - D) of the pending unit (the other half: slot 1 - h)
+        float rv[16], pv[16];
+        read_rows(qp, 1 - h, rv);
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 p = *reinterpret_cast<const float4*>(xch + xoff(h, r4));
-        pv[4 * r4 + 0] = p.x * (sacc[4 * r4 + 0] - rv[4 * r4 + 0]);
-        pv[4 * r4 + 1] = p.y * (sacc[4 * r4 + 1] - rv[4 * r4 + 1]);
-        pv[4 * r4 + 2] = p.z * (sacc[4 * r4 + 2] - rv[4 * r4 + 2]);
-        pv[4 * r4 + 3] = p.w * (sacc[4 * r4 + 3] - rv[4 * r4 + 3]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 p = *reinterpret_cast<const float4*>(xch + xoff(1 - h, r4));
+          pv[4 * r4 + 0] = p.x * (dp_prev[4 * r4 + 0] - rv[4 * r4 + 0]);
+          pv[4 * r4 + 1] = p.y * (dp_prev[4 * r4 + 1] - rv[4 * r4 + 1]);
+          pv[4 * r4 + 2] = p.z * (dp_prev[4 * r4 + 2] - rv[4 * r4 + 2]);
+          pv[4 * r4 + 3] = p.w * (dp_prev[4 * r4 + 3] - rv[4 * r4 + 3]);
+        }
+        frag fr[US];
+        to_frags(pv, fr);
+        accumulate(qp, 1 - h, fr);
       }
+      // dP = dO V^T of this unit
+      f32x16 pacc = {};
+#pragma unroll
+      for (int st = 0; st < C::QK_STEPS; ++st) pacc = E::mfma(op[st], bop[st], pacc);
+      dp_prev = pacc;
+      publish();
+      if (next) read_ops(qn, hn, op);
     }
-    // operand fragments of P or dS: k-step u covers queries h*32 + u*KSTEP + g*KPL + e =
-    // registers u*KPL + e
-    frag fr[US];
-#pragma unroll
-    for (int u = 0; u < US; ++u) {
-      if constexpr (KPL == 1) {
-        fr[u] = pv[u];
-      } else {
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) fr[u][e] = E::from_float(pv[u * KPL + e]);
-      }
-    }
-    if (next) read_ops(qn, hn, op);
-    // dV^T += dO^T P or dK^T += Q^T dS over the unit's queries
-#pragma unroll
-    for (int u = 0; u < US; ++u)
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-        acc[db] = E::mfma(tr_operand(qt + tr_region, off_tq[db], (h * 32 + u * KSTEP) * C::ROW_BYTES),
-                          fr[u], acc[db]);
   };
 
   // ---- the walk over the key block's query tiles ---------------------------------------------
   // Tile t sits in buffer t % 2.  The barrier of a tile's second unit also publishes tile t+1,
-  // committed just before it into the buffer tile t-1 used (every wave has passed the first
-  // unit's barrier of tile t, so none still reads tile t-1); tile t+2 is then loaded.
+  // committed just before it into the buffer tile t-1 used (after the first unit's barrier of
+  // tile t no wave reads tile t-1: the dS wave finished its lagging unit of tile t-1 before that
+  // barrier); tile t+2 is then loaded.
+  // The walk is written out once per role (same barriers in the same order), so that neither
+  // role's loop carries the other's registers.
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
-  int entry = 0;
-  frag op[C::QK_STEPS];
-  if (cnt > 0) {
-    entry = __builtin_amdgcn_readfirstlane(lst[0]);
-    load_tile(entry);
+  {
+    const int e0 = __builtin_amdgcn_readfirstlane(lst[0]);
+    load_tile(e0);
     wait_vmem();
     commit_tile(0);
     __syncthreads();
     if (cnt > 1) load_tile(__builtin_amdgcn_readfirstlane(lst[1]));
-    read_ops(bufp(0), 0, op);
   }
-  for (int t = 0; t < cnt; ++t) {
-    const int b = t & 1;
-    const bool test = (entry & 1) || ragged_block;
-    const uint64_t mrow = test ? tile_row_mask((entry >> 1) * C::BM) : 0ull;
-    const unsigned char* qt = bufp(b);
-    unit(qt, H0{}, test, mrow, [] { __syncthreads(); }, op, true, qt, 1);
-    const bool more = t + 1 < cnt;
-    unit(qt, H1{}, test, mrow, [&] {
-      if (more) {
-        wait_vmem();       // tile t+1 is in this wave's registers
-        commit_tile(b ^ 1);
-      }
-      __syncthreads();
-      if (t + 2 < cnt) load_tile(__builtin_amdgcn_readfirstlane(lst[t + 2]));
-    }, op, more, bufp(b ^ 1), 0);
-    if (more) entry = __builtin_amdgcn_readfirstlane(lst[t + 1]);
+  f32x16 dp_prev = {};  // dS wave: dP of the pending unit
+  auto walk = [&](auto role) {
+    int entry = __builtin_amdgcn_readfirstlane(lst[0]);
+    frag op[C::QK_STEPS];
+    read_ops(bufp(0), 0, op);
+    for (int t = 0; t < cnt; ++t) {
+      const int b = t & 1;
+      const bool test = (entry & 1) || ragged_block;
+      const uint64_t mrow = test ? tile_row_mask((entry >> 1) * C::BM) : 0ull;
+      const unsigned char* qt = bufp(b);
+      step(role, qt, H0{}, test, mrow, [] { __syncthreads(); }, op, dp_prev, true, qt, 1,
+           bufp(b ^ 1), t > 0);
+      const bool more = t + 1 < cnt;
+      step(role, qt, H1{}, test, mrow, [&] {
+        if (more) {
+          wait_vmem();       // tile t+1 is in this wave's registers
+          commit_tile(b ^ 1);
+        }
+        __syncthreads();
+        if (t + 2 < cnt) load_tile(__builtin_amdgcn_readfirstlane(lst[t + 2]));
+      }, op, dp_prev, more, bufp(b ^ 1), 0, qt, true);
+      if (more) entry = __builtin_amdgcn_readfirstlane(lst[t + 1]);
+    }
+  };
+  if (dsw)
+    walk(std::true_type{});
+  else
+    walk(std::false_type{});
+  // the dS wave's last pending unit: the second half of the last tile
+  if (dsw) {
+    const unsigned char* ql = bufp((cnt - 1) & 1);
+    float rv[16], pv[16];
+    read_rows(ql, 1, rv);
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 p = *reinterpret_cast<const float4*>(xch + xoff(1, r4));
+      pv[4 * r4 + 0] = p.x * (dp_prev[4 * r4 + 0] - rv[4 * r4 + 0]);
+      pv[4 * r4 + 1] = p.y * (dp_prev[4 * r4 + 1] - rv[4 * r4 + 1]);
+      pv[4 * r4 + 2] = p.z * (dp_prev[4 * r4 + 2] - rv[4 * r4 + 2]);
+      pv[4 * r4 + 3] = p.w * (dp_prev[4 * r4 + 3] - rv[4 * r4 + 3]);
+    }
+    frag fr[US];
+    to_frags(pv, fr);
+    accumulate(ql, 1, fr);
   }
 
   if (key_ok) {
