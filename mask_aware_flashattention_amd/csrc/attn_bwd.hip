@@ -350,8 +350,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
     int entry = __builtin_amdgcn_readfirstlane(lst[0]);
     frag op[C::QK_STEPS];
     read_ops(bufp(0), 0, op);
-    for (int t = 0; t < cnt; ++t) {
-      const int b = t & 1;
+    // tile t in buffer bc (a compile-time constant, so LDS offsets fold into the instructions)
+    auto tile = [&](const int t, auto bc) {
+      constexpr int b = decltype(bc)::value;
       const bool test = (entry & 1) || ragged_block;
       const uint64_t mrow = test ? tile_row_mask((entry >> 1) * C::BM) : 0ull;
       const unsigned char* qt = bufp(b);
@@ -367,7 +368,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
         if (t + 2 < cnt) load_tile(__builtin_amdgcn_readfirstlane(lst[t + 2]));
       }, op, dp_prev, more, bufp(b ^ 1), 0, qt, true);
       if (more) entry = __builtin_amdgcn_readfirstlane(lst[t + 1]);
+    };
+    int t = 0;
+    for (; t + 1 < cnt; t += 2) {
+      tile(t, std::integral_constant<int, 0>{});
+      tile(t + 1, std::integral_constant<int, 1>{});
     }
+    if (t < cnt) tile(t, std::integral_constant<int, 0>{});
   };
   if (dsw)
     walk(std::true_type{});
