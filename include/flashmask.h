@@ -114,6 +114,50 @@ int32_t flashmask_bwd(const fm_shape* shape, const void* Q, const void* K, const
                       void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Interface variants of the two attention calls: strided tensors, grouped key/value heads and
+ * per-batch or per-head mask vectors.  The pages do not describe these; they are the usual
+ * interface of attention libraries and change no arithmetic: every output equals what the
+ * calls above return on the same per-(batch, head) data.
+ *
+ * fm_layout:
+ *   B, H, nq, nk, d, dtype  as in fm_shape; H_kv key/value heads (1 <= H_kv, H % H_kv == 0):
+ *                           query head h reads key/value head h / (H / H_kv).
+ *   q_stride[3]             element strides (batch, head, row) of Q, O, dQ and dO; the d axis is
+ *                           contiguous.  Contiguous [B][H][nq][d] is {H*nq*d, nq*d, d}.
+ *   kv_stride[3]            the same for K, V, dK and dV ([B][H_kv][nk][d] when contiguous).
+ *   mask_b, mask_h          the four vectors hold mask_b * mask_h sets of nk int32 each
+ *                           (set s at offset s*nk); batch b, head h uses set
+ *                           (mask_b > 1 ? b : 0) * mask_h + (mask_h > 1 ? h : 0).
+ *                           mask_b is 1 or B, mask_h is 1 or H.
+ * Requirements (FM_ERR_SHAPE unless noted): strides >= 0, row strides >= d, every row
+ * start 16-byte aligned (stride * element size a multiple of 16, FM_ERR_ALIGN); per batch and
+ * head the rows span less than 4 GiB: (nq-1)*q_stride[2] + d elements (and for the backward
+ * also (H/H_kv - 1)*q_stride[1] more, with H/H_kv <= 256), (nk-1)*kv_stride[2] + d elements.
+ * Distinct outputs must not overlap each other or the inputs (not checked).  LSE stays
+ * contiguous float32 [B][H][nq].  In the backward dK and dV of a key/value head sum the
+ * gradients of its H/H_kv query heads, still without atomics and deterministic.
+ * Workspaces grow with the number of mask sets (lists per set).
+ */
+typedef struct {
+  int32_t B, H, H_kv, nq, nk, d;
+  int32_t dtype; /* fm_dtype */
+  int32_t mask_b, mask_h;
+  int64_t q_stride[3];
+  int64_t kv_stride[3];
+} fm_layout;
+
+size_t flashmask_fwd_ex_workspace_bytes(const fm_layout* layout);
+int32_t flashmask_fwd_ex(const fm_layout* layout, const void* Q, const void* K, const void* V,
+                         const int32_t* LTS, const int32_t* LTE, const int32_t* UTS,
+                         const int32_t* UTE, float scale, void* O, float* LSE, void* ws,
+                         size_t ws_bytes, void* stream);
+size_t flashmask_bwd_ex_workspace_bytes(const fm_layout* layout);
+int32_t flashmask_bwd_ex(const fm_layout* layout, const void* Q, const void* K, const void* V,
+                         const void* O, const void* dO, const float* LSE, const int32_t* LTS,
+                         const int32_t* LTE, const int32_t* UTS, const int32_t* UTE, float scale,
+                         void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Rank-local vectors by clip-shift-max.  "FlashMask-3: Efficient and Expressive Mask-Aware
  * Distributed Attention", abstract (zero-communication mask localisation); "FlashMask-3 sends
  * each GPU its mask ...", clip-shift-max paragraph (with Theorem 1).

@@ -8,9 +8,11 @@ from ._lib import FlashMaskError, load as load_library  # noqa: F401
 from .api import (  # noqa: F401
     block_order,
     bwd,
+    bwd_ex,
     bwd_workspace_bytes,
     classify,
     fwd,
+    fwd_ex,
     fwd_workspace_bytes,
     localize,
     prune_chunks,

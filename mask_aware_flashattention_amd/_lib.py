@@ -26,6 +26,12 @@ class FmShape(ctypes.Structure):
                 ("dtype", c_i32)]
 
 
+class FmLayout(ctypes.Structure):
+    _fields_ = [("B", c_i32), ("H", c_i32), ("H_kv", c_i32), ("nq", c_i32), ("nk", c_i32),
+                ("d", c_i32), ("dtype", c_i32), ("mask_b", c_i32), ("mask_h", c_i32),
+                ("q_stride", ctypes.c_int64 * 3), ("kv_stride", ctypes.c_int64 * 3)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "flashmask_strerror": (ctypes.c_char_p, [c_i32]),
@@ -46,6 +52,13 @@ SIGNATURES = {
                                        ctypes.c_size_t, c_p]),
     "flashmask_classify": (c_i32, [c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_p, c_p,
                                    c_p, c_p, c_p, c_p, ctypes.c_size_t, c_p]),
+    "flashmask_fwd_ex_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FmLayout)]),
+    "flashmask_fwd_ex": (c_i32, [ctypes.POINTER(FmLayout), c_p, c_p, c_p, c_p, c_p, c_p, c_p,
+                                 ctypes.c_float, c_p, c_p, c_p, ctypes.c_size_t, c_p]),
+    "flashmask_bwd_ex_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FmLayout)]),
+    "flashmask_bwd_ex": (c_i32, [ctypes.POINTER(FmLayout), c_p, c_p, c_p, c_p, c_p, c_p, c_p,
+                                 c_p, c_p, c_p, ctypes.c_float, c_p, c_p, c_p, c_p,
+                                 ctypes.c_size_t, c_p]),
 }
 
 _lib = None

@@ -12,7 +12,7 @@ import math
 import torch
 
 from . import _lib
-from ._lib import FmShape, check
+from ._lib import FmLayout, FmShape, check
 
 _DTYPES = {torch.bfloat16: _lib.FM_BF16, torch.float32: _lib.FM_FP32}
 
@@ -108,6 +108,93 @@ def bwd(q, k, v, o, do, lse, lts, lte, uts, ute, scale=None, *, workspace=None, 
                            ctypes.c_float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
                            ws.numel(), _stream(q.device))
     check(st, "flashmask_bwd")
+    return dq, dk, dv
+
+
+def _layout(q, k, v, vec):
+    """fm_layout of strided q [B,H,nq,d] and k, v [B,H_kv,nk,d] views and mask vectors of shape
+    [nk] (shared), [H, nk] (per head) or [mask_b, mask_h, nk] with mask_b in {1, B} and mask_h
+    in {1, H}."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B, H, nq, d] and k, v [B, H_kv, nk, d]")
+    B, H, nq, d = q.shape
+    Hkv, nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d or v.shape != k.shape or v.stride() != k.stride():
+        raise ValueError("k and v must have equal shapes [B, H_kv, nk, d] and equal strides")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("dtype must be bfloat16 or float32, the same for q, k, v")
+    if q.stride(3) != 1 or k.stride(3) != 1:
+        raise ValueError("the d axis must be contiguous")
+    if vec.dim() == 1:
+        mb, mh = 1, 1
+    elif vec.dim() == 2:
+        mb, mh = 1, vec.shape[0]
+    elif vec.dim() == 3:
+        mb, mh = vec.shape[0], vec.shape[1]
+    else:
+        raise ValueError("mask vectors must be [nk], [H, nk] or [mask_b, mask_h, nk]")
+    lay = FmLayout()
+    lay.B, lay.H, lay.H_kv, lay.nq, lay.nk, lay.d = B, H, Hkv, nq, nk, d
+    lay.dtype, lay.mask_b, lay.mask_h = _DTYPES[q.dtype], mb, mh
+    for i in range(3):
+        lay.q_stride[i] = q.stride(i)
+        lay.kv_stride[i] = k.stride(i)
+    return lay
+
+
+def _vector_sets(lts, lte, uts, ute, nk):
+    for x in (lts, lte, uts, ute):
+        if x.dtype != torch.int32 or x.shape[-1] != nk or x.shape != lts.shape:
+            raise ValueError(f"mask vectors must be int32 [..., {nk}] of one shape")
+        if not x.is_cuda or not x.is_contiguous():
+            raise ValueError("mask vectors must be contiguous device tensors")
+
+
+def _like_strided(t, like):
+    """Empty tensor with like's shape and strides (the layout the extended calls require)."""
+    return torch.empty_strided(like.shape, like.stride(), dtype=like.dtype, device=like.device)
+
+
+def fwd_ex(q, k, v, lts, lte, uts, ute, scale=None, *, out=None, lse=None, workspace=None):
+    """Forward on strided views: q [B,H,nq,d], k/v [B,H_kv,nk,d] (H_kv divides H: grouped
+    heads), mask vectors [nk], [H, nk] or [mask_b, mask_h, nk].  O has q's strides; LSE is
+    contiguous float32 [B,H,nq]."""
+    lib = _lib.load()
+    lay = _layout(q, k, v, lts)
+    _vector_sets(lts, lte, uts, ute, lay.nk)
+    if scale is None:
+        scale = 1.0 / math.sqrt(lay.d)
+    o = _like_strided(None, q) if out is None else out
+    if o.stride() != q.stride():
+        raise ValueError("out must have q's strides")
+    lse_t = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
+    nbytes = lib.flashmask_fwd_ex_workspace_bytes(ctypes.byref(lay))
+    ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    st = lib.flashmask_fwd_ex(ctypes.byref(lay), _ptr(q), _ptr(k), _ptr(v), _ptr(lts), _ptr(lte),
+                              _ptr(uts), _ptr(ute), ctypes.c_float(scale), _ptr(o), _ptr(lse_t),
+                              _ptr(ws), ws.numel(), _stream(q.device))
+    check(st, "flashmask_fwd_ex")
+    return o, lse_t
+
+
+def bwd_ex(q, k, v, o, do, lse, lts, lte, uts, ute, scale=None, *, workspace=None):
+    """dQ, dK, dV on strided views (see fwd_ex); o, do and dQ share q's strides, dK and dV k's.
+    With grouped heads dK and dV of a key/value head sum over its query heads."""
+    lib = _lib.load()
+    lay = _layout(q, k, v, lts)
+    _vector_sets(lts, lte, uts, ute, lay.nk)
+    if o.stride() != q.stride() or do.stride() != q.stride():
+        raise ValueError("o and do must have q's strides")
+    if scale is None:
+        scale = 1.0 / math.sqrt(lay.d)
+    dq, dk, dv = _like_strided(None, q), _like_strided(None, k), _like_strided(None, v)
+    nbytes = lib.flashmask_bwd_ex_workspace_bytes(ctypes.byref(lay))
+    ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    st = lib.flashmask_bwd_ex(ctypes.byref(lay), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                              _ptr(lse), _ptr(lts), _ptr(lte), _ptr(uts), _ptr(ute),
+                              ctypes.c_float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                              ws.numel(), _stream(q.device))
+    check(st, "flashmask_bwd_ex")
     return dq, dk, dv
 
 

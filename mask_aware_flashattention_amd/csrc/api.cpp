@@ -31,21 +31,6 @@ int32_t check_dtype(int32_t dtype, int32_t d) {
   return FM_OK;
 }
 
-// Shape checks shared by forward and backward; fills the tile geometry for (BM, BN).
-int32_t check_shape(const fm_shape* s, int32_t BM, int32_t BN, Geometry* g) {
-  if (!s) return FM_ERR_NULL;
-  const int32_t st = check_dtype(s->dtype, s->d);
-  if (st != FM_OK) return st;
-  if (s->B < 1 || s->H < 1 || s->nq < 1 || s->nk < 1) return FM_ERR_SHAPE;
-  if (s->nq > kMaxLen || s->nk > kMaxLen) return FM_ERR_SHAPE;
-  const int64_t n_qb = ceil_div(s->nq, BM), n_kb = ceil_div(s->nk, BN);
-  if (n_qb * n_kb > kMaxListEntries) return FM_ERR_SHAPE;
-  const int64_t bh = int64_t(s->B) * s->H;
-  if (bh * n_qb > 0x7fffffffLL || bh * n_kb > 0x7fffffffLL) return FM_ERR_SHAPE;
-  if (g) *g = Geometry{n_qb, n_kb};
-  return FM_OK;
-}
-
 int32_t check_vectors(const int32_t* a, const int32_t* b, const int32_t* c, const int32_t* d) {
   if (!a || !b || !c || !d) return FM_ERR_NULL;
   if (!aligned(a, 4) || !aligned(b, 4) || !aligned(c, 4) || !aligned(d, 4)) return FM_ERR_ALIGN;
@@ -58,17 +43,85 @@ int32_t check_scale(float scale) {
 
 fm::TileShape tiles(int32_t dtype) { return fm::tile_shape(dtype); }
 
+inline int64_t elem_size(int32_t dtype) { return dtype == FM_BF16 ? 2 : 4; }
+
+// Contiguous layout of an fm_shape: [B][H][n][d] tensors, H key/value heads, one mask set.
+fm_layout from_shape(const fm_shape* s) {
+  fm_layout l;
+  l.B = s->B;
+  l.H = s->H;
+  l.H_kv = s->H;
+  l.nq = s->nq;
+  l.nk = s->nk;
+  l.d = s->d;
+  l.dtype = s->dtype;
+  l.mask_b = 1;
+  l.mask_h = 1;
+  l.q_stride[0] = int64_t(s->H) * s->nq * s->d;
+  l.q_stride[1] = int64_t(s->nq) * s->d;
+  l.q_stride[2] = s->d;
+  l.kv_stride[0] = int64_t(s->H) * s->nk * s->d;
+  l.kv_stride[1] = int64_t(s->nk) * s->d;
+  l.kv_stride[2] = s->d;
+  return l;
+}
+
+fm::Layout to_internal(const fm_layout* l) {
+  return fm::Layout{l->B,           l->H,           l->H / l->H_kv,
+                    l->q_stride[0], l->q_stride[1], l->q_stride[2],
+                    l->kv_stride[0], l->kv_stride[1], l->kv_stride[2],
+                    l->mask_b,      l->mask_h,      l->nk};
+}
+
+inline int32_t mask_sets(const fm_layout* l) { return l->mask_b * l->mask_h; }
+
+// Layout checks shared by forward and backward (bwd: the dK/dV kernel also spans the query
+// heads of a group); fills the tile geometry for (BM, BN).
+int32_t check_layout(const fm_layout* l, int32_t BM, int32_t BN, bool bwd, Geometry* g) {
+  if (!l) return FM_ERR_NULL;
+  const int32_t st = check_dtype(l->dtype, l->d);
+  if (st != FM_OK) return st;
+  if (l->B < 1 || l->H < 1 || l->H_kv < 1 || l->nq < 1 || l->nk < 1) return FM_ERR_SHAPE;
+  if (l->H % l->H_kv != 0) return FM_ERR_SHAPE;
+  if (l->nq > kMaxLen || l->nk > kMaxLen) return FM_ERR_SHAPE;
+  if ((l->mask_b != 1 && l->mask_b != l->B) || (l->mask_h != 1 && l->mask_h != l->H))
+    return FM_ERR_SHAPE;
+  const int64_t n_qb = ceil_div(l->nq, BM), n_kb = ceil_div(l->nk, BN);
+  if (n_qb * n_kb > kMaxListEntries) return FM_ERR_SHAPE;
+  const int64_t bh = int64_t(l->B) * l->H;
+  if (bh * n_qb > 0x7fffffffLL || bh * n_kb > 0x7fffffffLL) return FM_ERR_SHAPE;
+  const int64_t es = elem_size(l->dtype);
+  for (int i = 0; i < 3; ++i) {
+    if (l->q_stride[i] < 0 || l->kv_stride[i] < 0) return FM_ERR_SHAPE;
+    if (l->q_stride[i] > (int64_t(1) << 40) || l->kv_stride[i] > (int64_t(1) << 40)) return FM_ERR_SHAPE;
+  }
+  if (l->q_stride[2] < l->d || l->kv_stride[2] < l->d) return FM_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i)
+    if ((l->q_stride[i] * es) % 16 != 0 || (l->kv_stride[i] * es) % 16 != 0) return FM_ERR_ALIGN;
+  // Every buffer a kernel addresses with 32-bit offsets stays below 4 GiB.
+  const int64_t G = l->H / l->H_kv;
+  int64_t q_span = ((int64_t)(l->nq - 1) * l->q_stride[2] + l->d) * es;
+  if (bwd) {
+    if (G > 256) return FM_ERR_SHAPE;
+    q_span += (G - 1) * l->q_stride[1] * es;
+  }
+  const int64_t k_span = ((int64_t)(l->nk - 1) * l->kv_stride[2] + l->d) * es;
+  if (q_span >= (int64_t(1) << 32) || k_span >= (int64_t(1) << 32)) return FM_ERR_SHAPE;
+  if (g) *g = Geometry{n_qb, n_kb};
+  return FM_OK;
+}
+
 // Forward workspace: key-block min/max, query-block lists and the longest-first block order.
 struct FwdWs {
   size_t mm, qcnt, qlist, order, total;
 };
-FwdWs fwd_layout(const Geometry& g) {
+FwdWs fwd_layout(const Geometry& g, int64_t sets = 1) {
   FwdWs w;
   w.mm = 0;
-  w.qcnt = w.mm + round_up(sizeof(int32_t) * 8 * g.n_kb);
-  w.qlist = w.qcnt + round_up(sizeof(int32_t) * g.n_qb);
-  w.order = w.qlist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb);
-  w.total = w.order + round_up(sizeof(int32_t) * g.n_qb);
+  w.qcnt = w.mm + round_up(sizeof(int32_t) * 8 * g.n_kb * sets);
+  w.qlist = w.qcnt + round_up(sizeof(int32_t) * g.n_qb * sets);
+  w.order = w.qlist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb * sets);
+  w.total = w.order + round_up(sizeof(int32_t) * g.n_qb * sets);
   return w;
 }
 
@@ -78,18 +131,19 @@ FwdWs fwd_layout(const Geometry& g) {
 struct BwdWs {
   size_t mm, kcnt, klist, mm_f, qcnt, qlist, korder, qorder, delta, lse2, total;
 };
-BwdWs bwd_layout(const fm_shape* s, const Geometry& g, const Geometry& gf) {
+BwdWs bwd_layout(const fm_layout* s, const Geometry& g, const Geometry& gf) {
   BwdWs w;
   const size_t rows = size_t(s->B) * s->H * s->nq;
+  const size_t sets = size_t(mask_sets(s));
   w.mm = 0;
-  w.kcnt = w.mm + round_up(sizeof(int32_t) * 8 * g.n_kb);
-  w.klist = w.kcnt + round_up(sizeof(int32_t) * g.n_kb);
-  w.mm_f = w.klist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb);
-  w.qcnt = w.mm_f + round_up(sizeof(int32_t) * 8 * gf.n_kb);
-  w.qlist = w.qcnt + round_up(sizeof(int32_t) * gf.n_qb);
-  w.korder = w.qlist + round_up(sizeof(int32_t) * gf.n_qb * gf.n_kb);
-  w.qorder = w.korder + round_up(sizeof(int32_t) * g.n_kb);
-  w.delta = w.qorder + round_up(sizeof(int32_t) * gf.n_qb);
+  w.kcnt = w.mm + round_up(sizeof(int32_t) * 8 * g.n_kb * sets);
+  w.klist = w.kcnt + round_up(sizeof(int32_t) * g.n_kb * sets);
+  w.mm_f = w.klist + round_up(sizeof(int32_t) * g.n_qb * g.n_kb * sets);
+  w.qcnt = w.mm_f + round_up(sizeof(int32_t) * 8 * gf.n_kb * sets);
+  w.qlist = w.qcnt + round_up(sizeof(int32_t) * gf.n_qb * sets);
+  w.korder = w.qlist + round_up(sizeof(int32_t) * gf.n_qb * gf.n_kb * sets);
+  w.qorder = w.korder + round_up(sizeof(int32_t) * g.n_kb * sets);
+  w.delta = w.qorder + round_up(sizeof(int32_t) * gf.n_qb * sets);
   w.lse2 = w.delta + round_up(sizeof(float) * rows);
   w.total = w.lse2 + round_up(sizeof(float) * rows);
   return w;
@@ -133,30 +187,31 @@ int32_t flashmask_tile_sizes(int32_t dtype, int32_t d, int32_t* BM_fwd, int32_t*
   return FM_OK;
 }
 
-size_t flashmask_fwd_workspace_bytes(const fm_shape* s) {
-  if (!s || check_dtype(s->dtype, s->d) != FM_OK) return 0;
-  const fm::TileShape t = tiles(s->dtype);
+size_t flashmask_fwd_ex_workspace_bytes(const fm_layout* l) {
+  if (!l || check_dtype(l->dtype, l->d) != FM_OK) return 0;
+  const fm::TileShape t = tiles(l->dtype);
   Geometry g;
-  if (check_shape(s, t.bm_fwd, t.bn_fwd, &g) != FM_OK) return 0;
-  return fwd_layout(g).total;
+  if (check_layout(l, t.bm_fwd, t.bn_fwd, false, &g) != FM_OK) return 0;
+  return fwd_layout(g, mask_sets(l)).total;
 }
 
-int32_t flashmask_fwd(const fm_shape* s, const void* Q, const void* K, const void* V,
-                      const int32_t* LTS, const int32_t* LTE, const int32_t* UTS,
-                      const int32_t* UTE, float scale, void* O, float* LSE, void* ws,
-                      size_t ws_bytes, void* stream) {
-  if (!s) return FM_ERR_NULL;
-  int32_t st = check_dtype(s->dtype, s->d);
+int32_t flashmask_fwd_ex(const fm_layout* l, const void* Q, const void* K, const void* V,
+                         const int32_t* LTS, const int32_t* LTE, const int32_t* UTS,
+                         const int32_t* UTE, float scale, void* O, float* LSE, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (!l) return FM_ERR_NULL;
+  int32_t st = check_dtype(l->dtype, l->d);
   if (st != FM_OK) return st;
-  const fm::TileShape t = tiles(s->dtype);
+  const fm::TileShape t = tiles(l->dtype);
   Geometry g;
-  if ((st = check_shape(s, t.bm_fwd, t.bn_fwd, &g)) != FM_OK) return st;
+  if ((st = check_layout(l, t.bm_fwd, t.bn_fwd, false, &g)) != FM_OK) return st;
   if (!Q || !K || !V || !O || !LSE) return FM_ERR_NULL;
   if ((st = check_vectors(LTS, LTE, UTS, UTE)) != FM_OK) return st;
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
     return FM_ERR_ALIGN;
   if ((st = check_scale(scale)) != FM_OK) return st;
-  const FwdWs L = fwd_layout(g);
+  const int32_t sets = mask_sets(l);
+  const FwdWs L = fwd_layout(g, sets);
   if (!ws || ws_bytes < L.total) return FM_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return FM_ERR_ALIGN;
 
@@ -168,39 +223,54 @@ int32_t flashmask_fwd(const fm_shape* s, const void* Q, const void* K, const voi
   int32_t* order = reinterpret_cast<int32_t*>(base + L.order);
   const fm::MaskVecs mv{LTS, LTE, UTS, UTE};
 
-  hipError_t e = fm::launch_block_minmax(mv, s->nk, t.bn_fwd, mm, hs);
+  hipError_t e = fm::launch_block_minmax(mv, l->nk, t.bn_fwd, mm, hs, sets, l->nk);
   if (e == hipSuccess)
-    e = fm::launch_classify(mm, (int32_t)g.n_kb, s->nq, t.bm_fwd, nullptr, qcnt, qlist, nullptr,
-                            nullptr, hs);
-  if (e == hipSuccess) e = fm::launch_block_order(qcnt, (int32_t)g.n_qb, order, hs);
+    e = fm::launch_classify(mm, (int32_t)g.n_kb, l->nq, t.bm_fwd, nullptr, qcnt, qlist, nullptr,
+                            nullptr, hs, sets);
+  if (e == hipSuccess) e = fm::launch_block_order(qcnt, (int32_t)g.n_qb, order, hs, sets);
   if (e == hipSuccess) {
     fm::FwdArgs a{Q,     K,     V,     mv,   O,    LSE,  qcnt, qlist, order, (int32_t)g.n_kb,
-                  s->B, s->H, s->nq, s->nk, scale};
-    e = fm::launch_attn_fwd(s->dtype, a, hs, g_fwd_begin, g_fwd_end);
+                  to_internal(l), l->nq, l->nk, scale};
+    e = fm::launch_attn_fwd(l->dtype, a, hs, g_fwd_begin, g_fwd_end);
   }
   return hip_status(e);
 }
 
-size_t flashmask_bwd_workspace_bytes(const fm_shape* s) {
-  if (!s || check_dtype(s->dtype, s->d) != FM_OK) return 0;
-  const fm::TileShape t = tiles(s->dtype);
-  Geometry g, gf;
-  if (check_shape(s, t.bm_bwd, t.bn_bwd, &g) != FM_OK) return 0;
-  if (check_shape(s, t.bm_fwd, t.bn_fwd, &gf) != FM_OK) return 0;
-  return bwd_layout(s, g, gf).total;
+size_t flashmask_fwd_workspace_bytes(const fm_shape* s) {
+  if (!s) return 0;
+  const fm_layout l = from_shape(s);
+  return flashmask_fwd_ex_workspace_bytes(&l);
 }
 
-int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const void* V,
-                      const void* O, const void* dO, const float* LSE, const int32_t* LTS,
-                      const int32_t* LTE, const int32_t* UTS, const int32_t* UTE, float scale,
-                      void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
+int32_t flashmask_fwd(const fm_shape* s, const void* Q, const void* K, const void* V,
+                      const int32_t* LTS, const int32_t* LTE, const int32_t* UTS,
+                      const int32_t* UTE, float scale, void* O, float* LSE, void* ws,
+                      size_t ws_bytes, void* stream) {
   if (!s) return FM_ERR_NULL;
-  int32_t st = check_dtype(s->dtype, s->d);
-  if (st != FM_OK) return st;
-  const fm::TileShape t = tiles(s->dtype);
+  const fm_layout l = from_shape(s);
+  return flashmask_fwd_ex(&l, Q, K, V, LTS, LTE, UTS, UTE, scale, O, LSE, ws, ws_bytes, stream);
+}
+
+size_t flashmask_bwd_ex_workspace_bytes(const fm_layout* l) {
+  if (!l || check_dtype(l->dtype, l->d) != FM_OK) return 0;
+  const fm::TileShape t = tiles(l->dtype);
   Geometry g, gf;
-  if ((st = check_shape(s, t.bm_bwd, t.bn_bwd, &g)) != FM_OK) return st;
-  if ((st = check_shape(s, t.bm_fwd, t.bn_fwd, &gf)) != FM_OK) return st;
+  if (check_layout(l, t.bm_bwd, t.bn_bwd, true, &g) != FM_OK) return 0;
+  if (check_layout(l, t.bm_fwd, t.bn_fwd, true, &gf) != FM_OK) return 0;
+  return bwd_layout(l, g, gf).total;
+}
+
+int32_t flashmask_bwd_ex(const fm_layout* l, const void* Q, const void* K, const void* V,
+                         const void* O, const void* dO, const float* LSE, const int32_t* LTS,
+                         const int32_t* LTE, const int32_t* UTS, const int32_t* UTE, float scale,
+                         void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
+  if (!l) return FM_ERR_NULL;
+  int32_t st = check_dtype(l->dtype, l->d);
+  if (st != FM_OK) return st;
+  const fm::TileShape t = tiles(l->dtype);
+  Geometry g, gf;
+  if ((st = check_layout(l, t.bm_bwd, t.bn_bwd, true, &g)) != FM_OK) return st;
+  if ((st = check_layout(l, t.bm_fwd, t.bn_fwd, true, &gf)) != FM_OK) return st;
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FM_ERR_NULL;
   if ((st = check_vectors(LTS, LTE, UTS, UTE)) != FM_OK) return st;
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
@@ -208,7 +278,8 @@ int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const voi
       !aligned(LSE, 4))
     return FM_ERR_ALIGN;
   if ((st = check_scale(scale)) != FM_OK) return st;
-  const BwdWs L = bwd_layout(s, g, gf);
+  const int32_t sets = mask_sets(l);
+  const BwdWs L = bwd_layout(l, g, gf);
   if (!ws || ws_bytes < L.total) return FM_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return FM_ERR_ALIGN;
 
@@ -225,28 +296,45 @@ int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const voi
   float* delta = reinterpret_cast<float*>(base + L.delta);
   float* lse2 = reinterpret_cast<float*>(base + L.lse2);
   const fm::MaskVecs mv{LTS, LTE, UTS, UTE};
+  const fm::Layout lay = to_internal(l);
 
-  hipError_t e = fm::launch_block_minmax(mv, s->nk, t.bn_bwd, mm, hs);
+  hipError_t e = fm::launch_block_minmax(mv, l->nk, t.bn_bwd, mm, hs, sets, l->nk);
   if (e == hipSuccess)
-    e = fm::launch_classify(mm, (int32_t)g.n_kb, s->nq, t.bm_bwd, nullptr, nullptr, nullptr, kcnt,
-                            klist, hs);
-  if (e == hipSuccess) e = fm::launch_block_minmax(mv, s->nk, t.bn_fwd, mm_f, hs);
+    e = fm::launch_classify(mm, (int32_t)g.n_kb, l->nq, t.bm_bwd, nullptr, nullptr, nullptr, kcnt,
+                            klist, hs, sets);
+  if (e == hipSuccess) e = fm::launch_block_minmax(mv, l->nk, t.bn_fwd, mm_f, hs, sets, l->nk);
   if (e == hipSuccess)
-    e = fm::launch_classify(mm_f, (int32_t)gf.n_kb, s->nq, t.bm_fwd, nullptr, qcnt, qlist, nullptr,
-                            nullptr, hs);
-  if (e == hipSuccess) e = fm::launch_block_order(kcnt, (int32_t)g.n_kb, korder, hs);
-  if (e == hipSuccess) e = fm::launch_block_order(qcnt, (int32_t)gf.n_qb, qorder, hs);
+    e = fm::launch_classify(mm_f, (int32_t)gf.n_kb, l->nq, t.bm_fwd, nullptr, qcnt, qlist, nullptr,
+                            nullptr, hs, sets);
+  if (e == hipSuccess) e = fm::launch_block_order(kcnt, (int32_t)g.n_kb, korder, hs, sets);
+  if (e == hipSuccess) e = fm::launch_block_order(qcnt, (int32_t)gf.n_qb, qorder, hs, sets);
   if (e == hipSuccess) {
     fm::BwdArgs a{Q,     K,    V,      O,    dO,   LSE,  mv,   dK, dV, delta, lse2, kcnt, klist,
-                  korder, (int32_t)g.n_qb, s->B, s->H, s->nq, s->nk, scale};
-    e = fm::launch_attn_bwd(s->dtype, a, hs, g_bwd_begin);
+                  korder, (int32_t)g.n_qb, lay, l->nq, l->nk, scale};
+    e = fm::launch_attn_bwd(l->dtype, a, hs, g_bwd_begin);
   }
   if (e == hipSuccess) {
     fm::DqArgs a{Q,    K,     V,     dO,    mv,   dQ,   delta, lse2, qcnt, qlist,
-                 qorder, (int32_t)gf.n_kb, s->B, s->H, s->nq, s->nk, scale};
-    e = fm::launch_attn_dq(s->dtype, a, hs, g_bwd_end);
+                 qorder, (int32_t)gf.n_kb, lay, l->nq, l->nk, scale};
+    e = fm::launch_attn_dq(l->dtype, a, hs, g_bwd_end);
   }
   return hip_status(e);
+}
+
+size_t flashmask_bwd_workspace_bytes(const fm_shape* s) {
+  if (!s) return 0;
+  const fm_layout l = from_shape(s);
+  return flashmask_bwd_ex_workspace_bytes(&l);
+}
+
+int32_t flashmask_bwd(const fm_shape* s, const void* Q, const void* K, const void* V,
+                      const void* O, const void* dO, const float* LSE, const int32_t* LTS,
+                      const int32_t* LTE, const int32_t* UTS, const int32_t* UTE, float scale,
+                      void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes, void* stream) {
+  if (!s) return FM_ERR_NULL;
+  const fm_layout l = from_shape(s);
+  return flashmask_bwd_ex(&l, Q, K, V, O, dO, LSE, LTS, LTE, UTS, UTE, scale, dQ, dK, dV, ws,
+                          ws_bytes, stream);
 }
 
 int32_t flashmask_localize(const int32_t* LTS_g, const int32_t* LTE_g, const int32_t* UTS_g,

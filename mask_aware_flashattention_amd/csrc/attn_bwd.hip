@@ -55,7 +55,9 @@ struct MaskRegs {
   int32_t lts, lte, uts, ute;
 };
 
-template <typename T, int D>
+// GQ: more than one query head per key/value head (a.L.G > 1); the G = 1 instantiation walks a
+// single list and needs no guard for rows past nq.
+template <typename T, int D, bool GQ>
 __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   using C = BwdTile<T, D>;
   using E = Elem<T>;
@@ -75,18 +77,29 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   const int kg = wv & 3;                                     // key group
   const bool dsw = wv >= 4;                                  // the dS wave of the pair
 
+  // The workgroup owns key block kb of key/value head hk of batch b; with G query heads per
+  // key/value head it walks the tile lists of all G heads in turn, accumulating into the same
+  // dK and dV registers (no atomics).
   const int n_kb = (a.nk + C::BN - 1) / C::BN;
   const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
-  const int bh = work / n_kb;
-  const int kb = a.order[work % n_kb];
+  // (every index here is the same for the whole workgroup; readfirstlane keeps it in scalar
+  // registers, and with it every pointer and buffer descriptor derived from it)
+  const int G = GQ ? a.L.G : 1;
+  const int Hk = a.L.H / G;
+  const int bhk = __builtin_amdgcn_readfirstlane(work / n_kb);
+  const int b = __builtin_amdgcn_readfirstlane(bhk / Hk);
+  const int hk = bhk - b * Hk, h0 = hk * G;
+  const int kb = __builtin_amdgcn_readfirstlane(a.order[(size_t)mask_set(a.L, b, h0) * n_kb + work % n_kb]);
   const int key = kb * C::BN + kg * 32 + l32;  // this lane's key (a column of S)
   const bool key_ok = key < a.nk;
-  const int cnt = a.kcnt[kb];
-  if (cnt == 0) {
+  const int64_t kbase = b * a.L.ks_b + hk * a.L.ks_h;
+  int total = 0;
+  for (int gi = 0; gi < G; ++gi) total += a.kcnt[(size_t)mask_set(a.L, b, h0 + gi) * n_kb + kb];
+  if (total == 0) {
     // No listed tile: every query row is masked for these keys, so dK = dV = 0.  Each lane
     // clears half of its key's row (128 bytes) in the tensor of its wave's role.
     if (key_ok) {
-      T* row = static_cast<T*>(wv >= 4 ? a.dk : a.dv) + ((size_t)bh * a.nk + key) * D;
+      T* row = static_cast<T*>(wv >= 4 ? a.dk : a.dv) + kbase + (size_t)key * a.L.ks_r;
       uint4* p = reinterpret_cast<uint4*>(row + g * (D / 2));
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -94,34 +107,23 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
     return;
   }
 
-  const T* __restrict__ Qp = static_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
-  const T* __restrict__ dOp = static_cast<const T*>(a.dout) + (size_t)bh * a.nq * D;
-  const T* __restrict__ Kp = static_cast<const T*>(a.k) + (size_t)bh * a.nk * D;
-  const T* __restrict__ Vp = static_cast<const T*>(a.v) + (size_t)bh * a.nk * D;
-  const float* __restrict__ lse2 = a.lse2 + (size_t)bh * a.nq;
-  const float* __restrict__ dlt = a.delta + (size_t)bh * a.nq;
-  const buf_rsrc qbuf = make_buf(Qp, (uint32_t)a.nq * C::ROW_BYTES);
-  const buf_rsrc dobuf = make_buf(dOp, (uint32_t)a.nq * C::ROW_BYTES);
-  const buf_rsrc kvbuf = make_buf(dsw ? Vp : Kp, (uint32_t)a.nk * C::ROW_BYTES);
-  const buf_rsrc lbuf = make_buf(lse2, (uint32_t)a.nq * sizeof(float));
-  const buf_rsrc dlbuf = make_buf(dlt, (uint32_t)a.nq * sizeof(float));
+  const T* __restrict__ Kp = static_cast<const T*>(a.k) + kbase;
+  const T* __restrict__ Vp = static_cast<const T*>(a.v) + kbase;
+  const uint32_t qrs = (uint32_t)a.L.qs_r * sizeof(T);  // row strides in bytes
+  const uint32_t krs = (uint32_t)a.L.ks_r * sizeof(T);
+  const buf_rsrc kvbuf = make_buf(dsw ? Vp : Kp, (uint32_t)(a.nk - 1) * krs + C::ROW_BYTES);
 
   // K (P wave) or V (dS wave) rows of this lane's key as B operands (k-step s: d = s*KSTEP +
   // g*KPL + 0..KPL); keys past nk read as zeros.
   frag bop[C::QK_STEPS];
 #pragma unroll
   for (int s = 0; s < C::QK_STEPS; ++s) {
-    const uint32_t off = (uint32_t)key * C::ROW_BYTES + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
+    const uint32_t off = (uint32_t)key * krs + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
     if constexpr (KPL == 8)
       bop[s] = __builtin_bit_cast(frag, buf_load16(kvbuf, off, 0));
     else
       bop[s] = __builtin_bit_cast(frag, buf_load4(kvbuf, off, 0));
   }
-  MaskRegs mk = {0, 0, 0, 0};  // this lane's key; past the last key every row is masked
-  if (key_ok) mk = {a.mask.lts[key], a.mask.lte[key], a.mask.uts[key], a.mask.ute[key]};
-  // Wait for these loads here: the main loop keeps tile loads in flight, and a wait the compiler
-  // would place there for a register loaded now would also wait for those.
-  wait_vmem();
   const bool ragged_block = (kb == n_kb - 1) && (a.nk % C::BN) != 0;
 
   // ---- per-lane LDS byte offsets, constant for the whole kernel ------------------------------
@@ -165,8 +167,60 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
 
-  const int32_t* __restrict__ lst = a.klist + (size_t)kb * a.list_stride;
   const float cexp = a.scale * kLog2e;
+
+  // The tiles of the G query heads of the group form one flat sequence: the list of head h0,
+  // then of h0 + 1, and so on (total tiles in all).  Q, dO and the LSE2 / D rows of all G heads
+  // lie in one buffer each, and a tile's head becomes part of its scalar offset.
+  const int64_t qbase = b * a.L.qs_b + h0 * a.L.qs_h;
+  const size_t rbase = ((size_t)b * a.L.H + h0) * a.nq;
+  const uint32_t qhs = (uint32_t)a.L.qs_h * sizeof(T);  // bytes from one head to the next
+  const uint32_t q_span = (uint32_t)(G - 1) * qhs + (uint32_t)(a.nq - 1) * qrs + C::ROW_BYTES;
+  const buf_rsrc qbuf = make_buf(static_cast<const T*>(a.q) + qbase, q_span);
+  const buf_rsrc dobuf = make_buf(static_cast<const T*>(a.dout) + qbase, q_span);
+  const buf_rsrc lbuf = make_buf(a.lse2 + rbase, (uint32_t)G * a.nq * sizeof(float));
+  const buf_rsrc dlbuf = make_buf(a.delta + rbase, (uint32_t)G * a.nq * sizeof(float));
+  // Position in the flat sequence: head gi of the group, index i in its list of c entries.
+  struct Cursor {
+    int gi, i, c;
+    const int32_t* l;
+  };
+  // Move u to the first head at or after u.gi whose list is not empty (u.gi = G past the end).
+  auto head_list = [&](Cursor& u) {
+    for (; u.gi < G; ++u.gi) {
+      const int set = mask_set(a.L, b, h0 + u.gi);
+      u.c = __builtin_amdgcn_readfirstlane(a.kcnt[(size_t)set * n_kb + kb]);
+      u.l = a.klist + ((size_t)set * n_kb + kb) * a.list_stride;
+      if (u.c > 0) return;
+    }
+  };
+  auto advance = [&](Cursor& u) {
+    if (++u.i == u.c && GQ) {
+      u.i = 0;
+      ++u.gi;
+      if (u.gi < G) head_list(u);
+    }
+  };
+  auto entry_of = [&](const Cursor& u) { return __builtin_amdgcn_readfirstlane(u.l[u.i]); };
+  // This lane's key's mask values for the tile's head; reloaded only when the head's mask set
+  // changes (never with one set per batch).
+  MaskRegs mk = {0, 0, 0, 0};  // past the last key every row is masked
+  int mk_set = -1;
+  auto load_mask = [&](int gi) {
+    const int set = mask_set(a.L, b, h0 + gi);
+    if (set == mk_set) return;
+    mk_set = set;
+    if (key_ok) {
+      const int64_t o = set * a.L.mask_stride + key;
+      mk = {a.mask.lts[o], a.mask.lte[o], a.mask.uts[o], a.mask.ute[o]};
+    }
+  };
+  Cursor first{0, 0, 0, nullptr};
+  head_list(first);
+  load_mask(first.gi);
+  // Wait for these loads here: the main loop keeps tile loads in flight, and a wait the compiler
+  // would place there for a register loaded now would also wait for those.
+  wait_vmem();
 
   // A tile's 64 rows of Q, then of dO, are 32 blocks of 1 KiB; wave w moves blocks 4w..4w+3
   // (waves 0-3 Q, 4-7 dO), lane l the 16-byte slot l of a block: row 4j + l/16 of its tensor,
@@ -176,18 +230,26 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   // a load in flight.
   uint4 stg[4];
   float strow = 0.0f;
-  auto load_tile = [&](int entry) {
-    const uint32_t tile_base = (uint32_t)(entry >> 1) * C::BM * C::ROW_BYTES;
+  // The buffers span all G heads, so rows past nq of one head are another head's rows: their
+  // offsets are moved to the buffer's end, where loads return zeros (dO = 0 and D = 0 make such a
+  // row contribute nothing).
+  auto load_tile = [&](int gi, int entry) {
+    const int q0 = (entry >> 1) * C::BM;
+    const uint32_t tile_base = (uint32_t)gi * qhs + (uint32_t)q0 * qrs;
     const buf_rsrc src = wv < 4 ? qbuf : dobuf;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * ((4 * wv + i) & 15) + (lane >> 4);
-      const uint32_t voff = (uint32_t)row * C::ROW_BYTES + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
+      const uint32_t voff = !GQ || q0 + row < a.nq
+                                ? (uint32_t)row * qrs + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16)
+                                : q_span - tile_base;
       stg[i] = buf_load16(src, voff, tile_base);
     }
     if (wv < 2) {
-      const uint32_t roff = (uint32_t)(entry >> 1) * C::BM * sizeof(float);
-      strow = __builtin_bit_cast(float, buf_load4(wv == 0 ? lbuf : dlbuf, (uint32_t)lane * sizeof(float), roff));
+      const uint32_t roff = ((uint32_t)gi * a.nq + (uint32_t)q0) * sizeof(float);
+      const uint32_t r_span = (uint32_t)G * a.nq * sizeof(float);
+      const uint32_t loff = !GQ || q0 + lane < a.nq ? (uint32_t)lane * sizeof(float) : r_span - roff;
+      strow = __builtin_bit_cast(float, buf_load4(wv == 0 ? lbuf : dlbuf, loff, roff));
     }
   };
   auto commit_tile = [&](int b) {
@@ -338,43 +400,62 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
   {
-    const int e0 = __builtin_amdgcn_readfirstlane(lst[0]);
-    load_tile(e0);
+    load_tile(first.gi, entry_of(first));
     wait_vmem();
     commit_tile(0);
     __syncthreads();
-    if (cnt > 1) load_tile(__builtin_amdgcn_readfirstlane(lst[1]));
+    if (total > 1) {
+      Cursor second = first;
+      advance(second);
+      load_tile(second.gi, entry_of(second));
+    }
   }
   f32x16 dp_prev = {};  // dS wave: dP of the pending unit
   auto walk = [&](auto role) {
-    int entry = __builtin_amdgcn_readfirstlane(lst[0]);
+    Cursor cur = first;        // the tile being walked
+    Cursor ahead = first;      // the tile two ahead, whose rows are loaded at the tile's end
+    advance(ahead);
+    if (total > 1) advance(ahead);
+    int entry = entry_of(cur);
     frag op[C::QK_STEPS];
     read_ops(bufp(0), 0, op);
     // tile t in buffer bc (a compile-time constant, so LDS offsets fold into the instructions)
     auto tile = [&](const int t, auto bc) {
       constexpr int b = decltype(bc)::value;
       const bool test = (entry & 1) || ragged_block;
-      const uint64_t mrow = test ? tile_row_mask((entry >> 1) * C::BM) : 0ull;
+      uint64_t mrow = 0ull;  // the row test belongs to the P wave only
+      if constexpr (!decltype(role)::value) {
+        if (test) {
+          load_mask(cur.gi);
+          mrow = tile_row_mask((entry >> 1) * C::BM);
+        }
+      }
       const unsigned char* qt = bufp(b);
       step(role, qt, H0{}, test, mrow, [] { __syncthreads(); }, op, dp_prev, true, qt, 1,
            bufp(b ^ 1), t > 0);
-      const bool more = t + 1 < cnt;
+      const bool more = t + 1 < total;
       step(role, qt, H1{}, test, mrow, [&] {
         if (more) {
           wait_vmem();       // tile t+1 is in this wave's registers
           commit_tile(b ^ 1);
         }
         __syncthreads();
-        if (t + 2 < cnt) load_tile(__builtin_amdgcn_readfirstlane(lst[t + 2]));
+        if (t + 2 < total) {
+          load_tile(ahead.gi, entry_of(ahead));
+          advance(ahead);
+        }
       }, op, dp_prev, more, bufp(b ^ 1), 0, qt, true);
-      if (more) entry = __builtin_amdgcn_readfirstlane(lst[t + 1]);
+      if (more) {
+        advance(cur);
+        entry = entry_of(cur);
+      }
     };
     int t = 0;
-    for (; t + 1 < cnt; t += 2) {
+    for (; t + 1 < total; t += 2) {
       tile(t, std::integral_constant<int, 0>{});
       tile(t + 1, std::integral_constant<int, 1>{});
     }
-    if (t < cnt) tile(t, std::integral_constant<int, 0>{});
+    if (t < total) tile(t, std::integral_constant<int, 0>{});
   };
   if (dsw)
     walk(std::true_type{});
@@ -382,7 +463,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
     walk(std::false_type{});
   // the dS wave's last pending unit: the second half of the last tile
   if (dsw) {
-    const unsigned char* ql = bufp((cnt - 1) & 1);
+    const unsigned char* ql = bufp((total - 1) & 1);
     float rv[16], pv[16];
     read_rows(ql, 1, rv);
 #pragma unroll
@@ -399,7 +480,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   }
 
   if (key_ok) {
-    T* dst = static_cast<T*>(dsw ? a.dk : a.dv) + ((size_t)bh * a.nk + key) * D;
+    T* dst = static_cast<T*>(dsw ? a.dk : a.dv) + kbase + (size_t)key * a.L.ks_r;
     const float sc = dsw ? a.scale : 1.0f;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
@@ -421,27 +502,34 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
 }
 
 // D_i = sum_d dO_id O_id (float32) and LSE_i * log2(e) (+inf for fully masked rows).  16 threads
-// per row, one 16-byte chunk of O and dO each.
+// per row, one 16-byte chunk of O and dO each; row r = (b*H + h)*nq + i.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
                                                       const T* __restrict__ dout,
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ delta,
-                                                      float* __restrict__ lse2, int64_t rows) {
+                                                      float* __restrict__ lse2, int64_t rows,
+                                                      Layout L, int32_t nq) {
   constexpr int CH = 16 / (int)sizeof(T);
   static_assert(D / CH == 16, "16 chunks per row");
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
   if (row >= rows) return;
-  const uint4 xo = *reinterpret_cast<const uint4*>(o + row * D + c * CH);
-  const uint4 xd = *reinterpret_cast<const uint4*>(dout + row * D + c * CH);
+  int64_t off = row * D + c * CH;  // contiguous [B][H][nq][d]
+  if (L.qs_r != D || L.qs_h != (int64_t)nq * D || L.qs_b != (int64_t)L.H * nq * D) {
+    const int64_t bh = row / nq, i = row - bh * nq;
+    const int64_t b = bh / L.H, h = bh - b * L.H;
+    off = b * L.qs_b + h * L.qs_h + i * L.qs_r + c * CH;
+  }
+  const uint4 xo = *reinterpret_cast<const uint4*>(o + off);
+  const uint4 xd = *reinterpret_cast<const uint4*>(dout + off);
   const T* eo = reinterpret_cast<const T*>(&xo);
   const T* ed = reinterpret_cast<const T*>(&xd);
   float acc = 0.0f;
 #pragma unroll
   for (int e = 0; e < CH; ++e) acc = fmaf((float)eo[e], (float)ed[e], acc);
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  for (int off2 = 8; off2 >= 1; off2 >>= 1) acc += __shfl_xor(acc, off2);
   if (c == 0) {
     delta[row] = acc;
     // LSE in log2 units; a fully masked row (LSE = -inf) gets +inf so that exp2(s - lse2) = 0
@@ -452,24 +540,25 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
 
 template <typename T, int D>
 hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin) {
-  const int64_t rows = (int64_t)a.B * a.H * a.nq;
+  const int64_t rows = (int64_t)a.L.B * a.L.H * a.nq;
   const int pre_grid = (int)((rows + 15) / 16);
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, stream,
                      static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.delta,
-                     a.lse2, rows);
+                     a.lse2, rows, a.L, a.nq);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
   using C = BwdTile<T, D>;
   const size_t smem = C::SMEM;
+  auto kernel = a.L.G > 1 ? &attn_bwd_kernel<T, D, true> : &attn_bwd_kernel<T, D, false>;
   // The main kernel uses more than 64 KiB of LDS; allow it on the current device.
-  err = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_kernel<T, D>),
+  err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
   const int64_t n_kb = (a.nk + C::BN - 1) / C::BN;
-  const int64_t grid = n_kb * a.B * a.H;
+  const int64_t grid = n_kb * a.L.B * (a.L.H / a.L.G);
   if (ev_begin) (void)hipEventRecord(ev_begin, stream);
-  hipLaunchKernelGGL((attn_bwd_kernel<T, D>), dim3((unsigned)grid), dim3(C::NT), smem, stream, a);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::NT), smem, stream, a);
   return hipGetLastError();
 }
 

@@ -69,27 +69,38 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
 
   const int n_qb = (a.nq + C::BM - 1) / C::BM;
   const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
-  const int bh = work / n_qb;
-  const int qb = a.order[work % n_qb];
+  // (readfirstlane keeps these workgroup-wide indices, and every pointer and buffer descriptor
+  // derived from them, in scalar registers)
+  const int bh = __builtin_amdgcn_readfirstlane(work / n_qb);
+  const int b = __builtin_amdgcn_readfirstlane(bh / a.L.H), head = bh - b * a.L.H;
+  const int set = mask_set(a.L, b, head);
+  const int qb = a.order[(size_t)set * n_qb + work % n_qb];
 
-  const T* __restrict__ Qp = static_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
-  const T* __restrict__ dOp = static_cast<const T*>(a.dout) + (size_t)bh * a.nq * D;
-  const T* __restrict__ Kp = static_cast<const T*>(a.k) + (size_t)bh * a.nk * D;
-  const T* __restrict__ Vp = static_cast<const T*>(a.v) + (size_t)bh * a.nk * D;
-  const buf_rsrc qbuf = make_buf(Qp, (uint32_t)a.nq * C::ROW_BYTES);
-  const buf_rsrc dobuf = make_buf(dOp, (uint32_t)a.nq * C::ROW_BYTES);
-  const buf_rsrc kbuf = make_buf(Kp, (uint32_t)a.nk * C::ROW_BYTES);
-  const buf_rsrc vbuf = make_buf(Vp, (uint32_t)a.nk * C::ROW_BYTES);
+  const int64_t qbase = b * a.L.qs_b + head * a.L.qs_h;
+  const int64_t kbase = b * a.L.ks_b + (head / a.L.G) * a.L.ks_h;
+  const T* __restrict__ Qp = static_cast<const T*>(a.q) + qbase;
+  const T* __restrict__ dOp = static_cast<const T*>(a.dout) + qbase;
+  const T* __restrict__ Kp = static_cast<const T*>(a.k) + kbase;
+  const T* __restrict__ Vp = static_cast<const T*>(a.v) + kbase;
+  const uint32_t qrs = (uint32_t)a.L.qs_r * sizeof(T);  // row strides in bytes
+  const uint32_t krs = (uint32_t)a.L.ks_r * sizeof(T);
+  const buf_rsrc qbuf = make_buf(Qp, (uint32_t)(a.nq - 1) * qrs + C::ROW_BYTES);
+  const buf_rsrc dobuf = make_buf(dOp, (uint32_t)(a.nq - 1) * qrs + C::ROW_BYTES);
+  const buf_rsrc kbuf = make_buf(Kp, (uint32_t)(a.nk - 1) * krs + C::ROW_BYTES);
+  const buf_rsrc vbuf = make_buf(Vp, (uint32_t)(a.nk - 1) * krs + C::ROW_BYTES);
+  const MaskVecs mask{a.mask.lts + set * a.L.mask_stride, a.mask.lte + set * a.L.mask_stride,
+                      a.mask.uts + set * a.L.mask_stride, a.mask.ute + set * a.L.mask_stride};
+  T* const dQp = static_cast<T*>(a.dq) + qbase;
 
   const int q0w = qb * C::BM + w * 32;  // first query row of this wave
   const int q_row = q0w + l32;          // this lane's query row
   const bool row_ok = q_row < a.nq;
-  const int cnt = a.qcnt[qb];
+  const int cnt = a.qcnt[(size_t)set * n_qb + qb];
   if (cnt == 0) {
     // No listed tile: the block's rows are fully masked, so dQ = 0 (each lane clears half of
     // its row, 128 bytes).
     if (row_ok) {
-      uint4* p = reinterpret_cast<uint4*>(static_cast<T*>(a.dq) + ((size_t)bh * a.nq + q_row) * D + g * (D / 2));
+      uint4* p = reinterpret_cast<uint4*>(dQp + (size_t)q_row * a.L.qs_r + g * (D / 2));
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -101,7 +112,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   frag qf[C::QK_STEPS], dof[C::QK_STEPS];
 #pragma unroll
   for (int s = 0; s < C::QK_STEPS; ++s) {
-    const uint32_t off = (uint32_t)q_row * C::ROW_BYTES + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
+    const uint32_t off = (uint32_t)q_row * qrs + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
     if constexpr (KPL == 8) {
       qf[s] = __builtin_bit_cast(frag, buf_load16(qbuf, off, 0));
       dof[s] = __builtin_bit_cast(frag, buf_load16(dobuf, off, 0));
@@ -114,7 +125,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   const float lse2 = row_ok ? a.lse2[(size_t)bh * a.nq + q_row] : INFINITY;
   const float dlt = row_ok ? a.delta[(size_t)bh * a.nq + q_row] : 0.0f;
 
-  const int32_t* __restrict__ lst = a.qlist + (size_t)qb * a.list_stride;
+  const int32_t* __restrict__ lst = a.qlist + ((size_t)set * n_qb + qb) * a.list_stride;
   const int last_kb = (a.nk - 1) / C::BN;
   const bool ragged = (a.nk % C::BN) != 0;
   const float cexp = a.scale * kLog2e;
@@ -154,12 +165,12 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   auto issue_tile = [&](int entry, auto bufc) {
     const int kb = entry >> 1;
     unsigned char* kt = bufp(bufc);
-    const uint32_t tile_base = (uint32_t)kb * C::BN * C::ROW_BYTES;
+    const uint32_t tile_base = (uint32_t)kb * C::BN * krs;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = 4 * w + i;
       const int row = 4 * j + (lane >> 4);
-      const uint32_t voff = (uint32_t)row * C::ROW_BYTES + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
+      const uint32_t voff = (uint32_t)row * krs + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
       buf_load_lds<16>(kbuf, kt + j * 1024, voff, tile_base);
       buf_load_lds<16>(vbuf, kt + C::TILE_BYTES + j * 1024, voff, tile_base);
     }
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
           const uint32_t upto_hi = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
           return upto_hi & ~((1u << lo) - 1u);  // lo < 32 here
         };
-        word = bits(a.mask.lts[jk], a.mask.lte[jk]) | bits(a.mask.uts[jk], a.mask.ute[jk]);
+        word = bits(mask.lts[jk], mask.lte[jk]) | bits(mask.uts[jk], mask.ute[jk]);
       }
       mwp(bufc)[w * C::BN + mkey] = word;
     }
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   if (it < cnt) body(it, std::integral_constant<int, 0>{});
 
   if (row_ok) {
-    T* orow = static_cast<T*>(a.dq) + ((size_t)bh * a.nq + q_row) * D;
+    T* orow = dQp + (size_t)q_row * a.L.qs_r;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -291,7 +302,7 @@ template <typename T, int D>
 hipError_t run_dq(const DqArgs& a, hipStream_t stream, hipEvent_t ev_end) {
   using C = DqTile<T, D>;
   const int64_t n_qb = (a.nq + C::BM - 1) / C::BM;
-  const int64_t grid = n_qb * a.B * a.H;
+  const int64_t grid = n_qb * a.L.B * a.L.H;
   hipLaunchKernelGGL((attn_dq_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   const hipError_t err = hipGetLastError();
   if (ev_end) (void)hipEventRecord(ev_end, stream);

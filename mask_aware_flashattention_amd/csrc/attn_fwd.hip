@@ -79,29 +79,39 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 
   const int n_qb = (a.nq + C::BM - 1) / C::BM;
   const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
-  const int bh = work / n_qb;
+  // (readfirstlane keeps these workgroup-wide indices, and every pointer and buffer descriptor
+  // derived from them, in scalar registers)
+  const int bh = __builtin_amdgcn_readfirstlane(work / n_qb);
+  const int b = __builtin_amdgcn_readfirstlane(bh / a.L.H), head = bh - b * a.L.H;
+  const int set = mask_set(a.L, b, head);
   // Query blocks in the order of a.order (longest lists first, neighbours kept together).
-  const int qb = a.order[work % n_qb];
+  const int qb = a.order[(size_t)set * n_qb + work % n_qb];
 
-  const T* __restrict__ Qp = static_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
-  const T* __restrict__ Kp = static_cast<const T*>(a.k) + (size_t)bh * a.nk * D;
-  const T* __restrict__ Vp = static_cast<const T*>(a.v) + (size_t)bh * a.nk * D;
-  const buf_rsrc qbuf = make_buf(Qp, (uint32_t)a.nq * C::ROW_BYTES);
-  const buf_rsrc kbuf = make_buf(Kp, (uint32_t)a.nk * C::ROW_BYTES);
-  const buf_rsrc vbuf = make_buf(Vp, (uint32_t)a.nk * C::ROW_BYTES);
+  const T* __restrict__ Qp = static_cast<const T*>(a.q) + b * a.L.qs_b + head * a.L.qs_h;
+  const T* __restrict__ Kp = static_cast<const T*>(a.k) + b * a.L.ks_b + (head / a.L.G) * a.L.ks_h;
+  const T* __restrict__ Vp = static_cast<const T*>(a.v) + b * a.L.ks_b + (head / a.L.G) * a.L.ks_h;
+  const uint32_t qrs = (uint32_t)a.L.qs_r * sizeof(T);  // row strides in bytes
+  const uint32_t krs = (uint32_t)a.L.ks_r * sizeof(T);
+  const buf_rsrc qbuf = make_buf(Qp, (uint32_t)(a.nq - 1) * qrs + C::ROW_BYTES);
+  const buf_rsrc kbuf = make_buf(Kp, (uint32_t)(a.nk - 1) * krs + C::ROW_BYTES);
+  const buf_rsrc vbuf = make_buf(Vp, (uint32_t)(a.nk - 1) * krs + C::ROW_BYTES);
+  const MaskVecs mask{a.mask.lts + set * a.L.mask_stride, a.mask.lte + set * a.L.mask_stride,
+                      a.mask.uts + set * a.L.mask_stride, a.mask.ute + set * a.L.mask_stride};
+  T* const Op = static_cast<T*>(a.o) + b * a.L.qs_b + head * a.L.qs_h;
+  float* const lse_row = a.lse + (size_t)bh * a.nq;
 
   const int q0w = qb * C::BM + w * 32;  // first query row of this wave
   const int q_row = q0w + l32;          // this lane's query row
   const bool row_ok = q_row < a.nq;
-  const int cnt = a.qcnt[qb];
+  const int cnt = a.qcnt[(size_t)set * n_qb + qb];
   if (cnt == 0) {
     // No listed tile: the block's rows are fully masked: O = 0, LSE = -inf (each lane clears
     // half of its row, 128 bytes).
     if (row_ok) {
-      uint4* p = reinterpret_cast<uint4*>(static_cast<T*>(a.o) + ((size_t)bh * a.nq + q_row) * D + g * (D / 2));
+      uint4* p = reinterpret_cast<uint4*>(Op + (size_t)q_row * a.L.qs_r + g * (D / 2));
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (g == 0) a.lse[(size_t)bh * a.nq + q_row] = -INFINITY;
+      if (g == 0) lse_row[q_row] = -INFINITY;
     }
     return;
   }
@@ -111,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   frag qf[C::QK_STEPS];
 #pragma unroll
   for (int s = 0; s < C::QK_STEPS; ++s) {
-    const uint32_t off = (uint32_t)q_row * C::ROW_BYTES + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
+    const uint32_t off = (uint32_t)q_row * qrs + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
     if constexpr (KPL == 8) {
       qf[s] = __builtin_bit_cast(frag, buf_load16(qbuf, off, 0));
     } else {
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     }
   }
 
-  const int32_t* __restrict__ lst = a.qlist + (size_t)qb * a.list_stride;
+  const int32_t* __restrict__ lst = a.qlist + ((size_t)set * n_qb + qb) * a.list_stride;
   const int last_kb = (a.nk - 1) / C::BN;
   const bool ragged = (a.nk % C::BN) != 0;
   const float cexp = a.scale * kLog2e;
@@ -153,10 +163,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   // stall in order on the full memory queue before any of them reaches its products.
   auto stage_part = [&](int entry, auto bufc, int i) {
     unsigned char* kt = bufp(bufc);
-    const uint32_t tile_base = (uint32_t)(entry >> 1) * C::BN * C::ROW_BYTES;
+    const uint32_t tile_base = (uint32_t)(entry >> 1) * C::BN * krs;
     const int j = 4 * w + i;
     const int row = 4 * j + (lane >> 4);
-    const uint32_t voff = (uint32_t)row * C::ROW_BYTES + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
+    const uint32_t voff = (uint32_t)row * krs + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16);
     buf_load_lds<16>(kbuf, kt + j * 1024, voff, tile_base);
     buf_load_lds<16>(vbuf, kt + C::TILE_BYTES + j * 1024, voff, tile_base);
   };
@@ -172,10 +182,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     const int jk = (entry >> 1) * C::BN + lane;
     m.live = jk < a.nk;  // keys past nk are masked for every row
     if (m.live) {
-      m.s0 = a.mask.lts[jk];
-      m.e0 = a.mask.lte[jk];
-      m.s1 = a.mask.uts[jk];
-      m.e1 = a.mask.ute[jk];
+      m.s0 = mask.lts[jk];
+      m.e0 = mask.lte[jk];
+      m.s1 = mask.uts[jk];
+      m.e1 = mask.ute[jk];
     }
     return m;
   };
@@ -324,9 +334,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   const float l = pair_sum32(l_run);
   if (row_ok) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    if (g == 0)
-      a.lse[(size_t)bh * a.nq + q_row] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
-    T* orow = static_cast<T*>(a.o) + ((size_t)bh * a.nq + q_row) * D;
+    if (g == 0) lse_row[q_row] = l > 0.0f ? (m_run + log2f(l)) * kLn2 : -INFINITY;
+    T* orow = Op + (size_t)q_row * a.L.qs_r;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -356,7 +365,7 @@ TileShape tile_shape(int dtype) {
 hipError_t launch_attn_fwd(int dtype, const FwdArgs& a, hipStream_t stream, hipEvent_t ev_begin,
                            hipEvent_t ev_end) {
   const int64_t n_qb = (a.nq + 127) / 128;
-  const int64_t grid = n_qb * a.B * a.H;
+  const int64_t grid = n_qb * a.L.B * a.L.H;
   if (ev_begin) (void)hipEventRecord(ev_begin, stream);
   if (dtype == 0)
     hipLaunchKernelGGL((attn_fwd_kernel<bf16, 128>), dim3((unsigned)grid), dim3(256), 0, stream, a);

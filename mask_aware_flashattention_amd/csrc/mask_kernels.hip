@@ -34,11 +34,19 @@ struct MaxOp {
   __device__ int32_t operator()(int32_t a, int32_t b) const { return a > b ? a : b; }
 };
 
-// One wave per key block; lanes stride over the block's keys.
-__global__ __launch_bounds__(256) void block_minmax_kernel(MaskVecs v, int32_t nk, int32_t BN,
-                                                           int32_t n_kb, int32_t* __restrict__ mm) {
+// One wave per key block; lanes stride over the block's keys.  blockIdx.y is the mask set:
+// vectors at offset set * vec_stride, output at mm + set * 8 * n_kb.
+__global__ __launch_bounds__(256) void block_minmax_kernel(MaskVecs v, int64_t vec_stride,
+                                                           int32_t nk, int32_t BN, int32_t n_kb,
+                                                           int32_t* __restrict__ mm) {
   const int kb = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (kb >= n_kb) return;
+  const int64_t set = blockIdx.y;
+  v.lts += set * vec_stride;
+  v.lte += set * vec_stride;
+  v.uts += set * vec_stride;
+  v.ute += set * vec_stride;
+  mm += set * 8 * n_kb;
   const int lane = lane_id();
   const int64_t j0 = (int64_t)kb * BN;
   const int64_t j1 = j0 + BN < nk ? j0 + BN : nk;
@@ -100,6 +108,7 @@ __device__ inline int lanes_below(uint64_t mask) {
 // Waves [0, row_waves) each own one query block and scan every key block (forward lists,
 // class matrix); the following waves each own one key block and scan every query block
 // (backward lists).  Compaction is a wave ballot + prefix count, so lists come out ascending.
+// blockIdx.y is the mask set: every input and output is offset by its per-set size.
 __global__ __launch_bounds__(256) void classify_kernel(const int32_t* __restrict__ mm, int32_t n_kb,
                                                        int32_t nq, int32_t BM, int32_t n_qb,
                                                        int32_t row_waves, int32_t col_waves,
@@ -110,6 +119,15 @@ __global__ __launch_bounds__(256) void classify_kernel(const int32_t* __restrict
                                                        int32_t* __restrict__ klist) {
   const int wid = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int lane = lane_id();
+  {
+    const int64_t set = blockIdx.y;
+    mm += set * 8 * n_kb;
+    if (cls) cls += set * n_qb * n_kb;
+    if (qcnt) qcnt += set * n_qb;
+    if (qlist) qlist += set * n_qb * n_kb;
+    if (kcnt) kcnt += set * n_kb;
+    if (klist) klist += set * n_kb * n_qb;
+  }
   if (wid < row_waves) {
     const int qb = wid;
     const int32_t r0 = qb * BM;
@@ -215,9 +233,12 @@ inline int grid_for(int64_t work, int threads, int cap) {
 // and a scan over threads gives each of its blocks its slot.
 constexpr int kOrderBuckets = 4;
 constexpr int kOrderThreads = 1024;
+// One workgroup per mask set (blockIdx.x): counts and order at offset set * n.
 __global__ __launch_bounds__(kOrderThreads) void block_order_kernel(const int32_t* __restrict__ cnt,
                                                                     int32_t n,
                                                                     int32_t* __restrict__ order) {
+  cnt += (int64_t)blockIdx.x * n;
+  order += (int64_t)blockIdx.x * n;
   constexpr int kWaves = kOrderThreads / kWave;
   __shared__ int32_t wmax[kWaves];
   __shared__ int32_t slot[kOrderBuckets][kOrderThreads];  // per-thread counts, then first slots
@@ -287,30 +308,32 @@ __global__ __launch_bounds__(kOrderThreads) void block_order_kernel(const int32_
 }  // namespace
 
 hipError_t launch_block_minmax(MaskVecs v, int32_t nk, int32_t BN, int32_t* mm,
-                               hipStream_t stream) {
+                               hipStream_t stream, int32_t sets, int64_t vec_stride) {
   const int32_t n_kb = (nk + BN - 1) / BN;
   const int grid = (n_kb + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL(block_minmax_kernel, dim3(grid), dim3(256), 0, stream, v, nk, BN, n_kb, mm);
+  hipLaunchKernelGGL(block_minmax_kernel, dim3(grid, sets), dim3(256), 0, stream, v, vec_stride, nk,
+                     BN, n_kb, mm);
   return hipGetLastError();
 }
 
 hipError_t launch_classify(const int32_t* mm, int32_t n_kb, int32_t nq, int32_t BM,
                            uint8_t* cls, int32_t* qcnt, int32_t* qlist, int32_t* kcnt,
-                           int32_t* klist, hipStream_t stream) {
+                           int32_t* klist, hipStream_t stream, int32_t sets) {
   const int32_t n_qb = (nq + BM - 1) / BM;
   const int32_t row_waves = (cls || qcnt || qlist) ? n_qb : 0;
   const int32_t col_waves = (kcnt && klist) ? n_kb : 0;
   const int64_t waves = (int64_t)row_waves + col_waves;
   if (waves == 0) return hipSuccess;
   const int grid = (int)((waves + kWavesPerBlock - 1) / kWavesPerBlock);
-  hipLaunchKernelGGL(classify_kernel, dim3(grid), dim3(256), 0, stream, mm, n_kb, nq, BM, n_qb,
-                     row_waves, col_waves, cls, qcnt, qlist, kcnt, klist);
+  hipLaunchKernelGGL(classify_kernel, dim3(grid, sets), dim3(256), 0, stream, mm, n_kb, nq, BM,
+                     n_qb, row_waves, col_waves, cls, qcnt, qlist, kcnt, klist);
   return hipGetLastError();
 }
 
-hipError_t launch_block_order(const int32_t* cnt, int32_t n, int32_t* order, hipStream_t stream) {
+hipError_t launch_block_order(const int32_t* cnt, int32_t n, int32_t* order, hipStream_t stream,
+                              int32_t sets) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(block_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, cnt, n, order);
+  hipLaunchKernelGGL(block_order_kernel, dim3(sets), dim3(kOrderThreads), 0, stream, cnt, n, order);
   return hipGetLastError();
 }
 

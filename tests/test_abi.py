@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -196,3 +196,90 @@ def test_prune_checks(lib):
     assert call(live=ctypes.c_void_p(0x200002)) == FM_ERR_ALIGN
     assert call(ws_bytes=767) == FM_ERR_WORKSPACE
     assert call(ws=NUL) == FM_ERR_WORKSPACE
+
+
+def layout(B=1, H=2, H_kv=None, nq=300, nk=200, d=128, dtype=0, mask_b=1, mask_h=1, qs=None,
+           ks=None):
+    l = _lib.FmLayout()
+    l.B, l.H, l.H_kv, l.nq, l.nk, l.d, l.dtype = B, H, H if H_kv is None else H_kv, nq, nk, d, dtype
+    l.mask_b, l.mask_h = mask_b, mask_h
+    hk = l.H_kv
+    for i, x in enumerate(qs or (H * nq * d, nq * d, d)):
+        l.q_stride[i] = x
+    for i, x in enumerate(ks or (hk * nk * d, nk * d, d)):
+        l.kv_stride[i] = x
+    return l
+
+
+def test_ex_workspace_matches_plain_and_scales_with_mask_sets(lib):
+    r = lambda x: -(-x // 256) * 256
+    assert (lib.flashmask_fwd_ex_workspace_bytes(ctypes.byref(layout()))
+            == lib.flashmask_fwd_workspace_bytes(ctypes.byref(shape())))
+    assert (lib.flashmask_bwd_ex_workspace_bytes(ctypes.byref(layout()))
+            == lib.flashmask_bwd_workspace_bytes(ctypes.byref(shape())))
+    n_qb, n_kb, sets = 3, 4, 2 * 2   # mask per batch and head, B = H = 2
+    l = layout(B=2, mask_b=2, mask_h=2)
+    assert lib.flashmask_fwd_ex_workspace_bytes(ctypes.byref(l)) == (
+        r(32 * n_kb * sets) + r(4 * n_qb * sets) + r(4 * n_qb * n_kb * sets) + r(4 * n_qb * sets))
+    n_qb, n_kb = 5, 2
+    f_qb, f_kb = 3, 4
+    rows = 2 * 2 * 300
+    want = (r(32 * n_kb * sets) + r(4 * n_kb * sets) + r(4 * n_qb * n_kb * sets)
+            + r(32 * f_kb * sets) + r(4 * f_qb * sets) + r(4 * f_qb * f_kb * sets)
+            + r(4 * n_kb * sets) + r(4 * f_qb * sets) + 2 * r(4 * rows))
+    assert lib.flashmask_bwd_ex_workspace_bytes(ctypes.byref(l)) == want
+    assert lib.flashmask_fwd_ex_workspace_bytes(None) == 0
+
+
+def fwd_ex(lib, l, q=P, vec=P, scale=0.1, ws=P, ws_bytes=0):
+    return lib.flashmask_fwd_ex(ctypes.byref(l) if l is not None else None, q, P, P, vec, vec, vec,
+                                vec, ctypes.c_float(scale), P2, P2, ws, ws_bytes, NUL)
+
+
+def bwd_ex(lib, l, dk=P2, scale=0.1, ws_bytes=0):
+    return lib.flashmask_bwd_ex(ctypes.byref(l), P, P, P, P, P, P2, P, P, P, P,
+                                ctypes.c_float(scale), P2, dk, P2, P, ws_bytes, NUL)
+
+
+def test_ex_layout_checks(lib):
+    assert fwd_ex(lib, None) == FM_ERR_NULL
+    assert fwd_ex(lib, layout(dtype=4)) == FM_ERR_DTYPE
+    assert fwd_ex(lib, layout(d=64)) == FM_ERR_UNSUPPORTED
+    assert fwd_ex(lib, layout()) == FM_ERR_WORKSPACE          # everything else valid
+    assert fwd_ex(lib, layout(H=4, H_kv=2)) == FM_ERR_WORKSPACE
+    assert fwd_ex(lib, layout(B=2, H=4, mask_b=2, mask_h=4)) == FM_ERR_WORKSPACE
+    shape_errors = [
+        dict(H=4, H_kv=3),                    # H_kv does not divide H
+        dict(H_kv=0),
+        dict(B=2, mask_b=3),                  # mask sets: 1 or B, 1 or H
+        dict(mask_h=3),
+        dict(qs=(2 * 300 * 128, 300 * 128, 120)),   # row stride below d
+        dict(ks=(-8, 200 * 128, 128)),               # negative stride
+        dict(nk=200, ks=(0, 0, 1 << 25)),            # K rows span 4 GiB or more
+        dict(nq=0),
+        dict(nk=(1 << 22) + 1),
+    ]
+    for kw in shape_errors:
+        assert fwd_ex(lib, layout(**kw)) == FM_ERR_SHAPE, kw
+    # every row start 16-byte aligned: strides * 2 bytes must be multiples of 16
+    assert fwd_ex(lib, layout(qs=(2 * 300 * 128, 300 * 128 + 4, 128))) == FM_ERR_ALIGN
+    assert fwd_ex(lib, layout(ks=(2 * 200 * 128, 200 * 128, 132))) == FM_ERR_ALIGN
+    assert fwd_ex(lib, layout(), q=NUL) == FM_ERR_NULL
+    assert fwd_ex(lib, layout(), q=MIS) == FM_ERR_ALIGN
+    assert fwd_ex(lib, layout(), vec=NUL) == FM_ERR_NULL
+    assert fwd_ex(lib, layout(), scale=float("nan")) == FM_ERR_VALUE
+    need = lib.flashmask_fwd_ex_workspace_bytes(ctypes.byref(layout()))
+    assert fwd_ex(lib, layout(), ws_bytes=need - 1) == FM_ERR_WORKSPACE
+    assert fwd_ex(lib, layout(), ws=NUL, ws_bytes=need) == FM_ERR_WORKSPACE
+
+
+def test_bwd_ex_checks(lib):
+    assert bwd_ex(lib, layout()) == FM_ERR_WORKSPACE
+    assert bwd_ex(lib, layout(H=4, H_kv=1)) == FM_ERR_WORKSPACE
+    assert bwd_ex(lib, layout(H=512, H_kv=1, nq=128, nk=128)) == FM_ERR_SHAPE  # group above 256
+    # the dK/dV kernel spans a group's query heads: (G-1) head strides + the rows < 4 GiB
+    assert fwd_ex(lib, layout(H=4, H_kv=1, qs=(0, 1 << 30, 128))) == FM_ERR_WORKSPACE
+    assert bwd_ex(lib, layout(H=4, H_kv=1, qs=(0, 1 << 30, 128))) == FM_ERR_SHAPE
+    assert bwd_ex(lib, layout(), dk=NUL) == FM_ERR_NULL
+    assert bwd_ex(lib, layout(), dk=MIS) == FM_ERR_ALIGN
+    assert bwd_ex(lib, layout(), scale=0.0) == FM_ERR_VALUE
