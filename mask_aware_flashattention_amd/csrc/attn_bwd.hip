@@ -6,7 +6,7 @@
 // partly masked tiles, as the forward; "FlashMask-3 sends each GPU its mask ...",
 // tile-classification paragraph).
 //
-//   K4 bwd_pre:  D_i = sum_d dO_id O_id and LSE_i * log2(e) per query row.
+//   K4 bwd_pre:  -D_i = -sum_d dO_id O_id and LSE_i * log2(e) per query row.
 //   K5 dK / dV:  one workgroup of 8 waves per key block of BN = 128 keys: 4 key groups of 32
 //                keys, and per key group a pair of waves on one SIMD that split the work:
 //                  the P wave keeps K rows in registers, computes S = Q K^T, P = exp2(S*scale*
@@ -365,23 +365,28 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
       accumulate(qt, h, fr);
     } else {
       if (pending) {
-        // dS = P (dP - D) of the pending unit (the other half: slot 1 - h)
-        float rv[16], pv[16];
-        read_rows(qp, 1 - h, rv);
+        // dS = P (dP - D) of the pending unit (the other half: slot 1 - h); dp_prev already
+        // holds dP - D
+        float pv[16];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const float4 p = *reinterpret_cast<const float4*>(xch + xoff(1 - h, r4));
-          pv[4 * r4 + 0] = p.x * (dp_prev[4 * r4 + 0] - rv[4 * r4 + 0]);
-          pv[4 * r4 + 1] = p.y * (dp_prev[4 * r4 + 1] - rv[4 * r4 + 1]);
-          pv[4 * r4 + 2] = p.z * (dp_prev[4 * r4 + 2] - rv[4 * r4 + 2]);
-          pv[4 * r4 + 3] = p.w * (dp_prev[4 * r4 + 3] - rv[4 * r4 + 3]);
+          pv[4 * r4 + 0] = p.x * dp_prev[4 * r4 + 0];
+          pv[4 * r4 + 1] = p.y * dp_prev[4 * r4 + 1];
+          pv[4 * r4 + 2] = p.z * dp_prev[4 * r4 + 2];
+          pv[4 * r4 + 3] = p.w * dp_prev[4 * r4 + 3];
         }
         frag fr[US];
         to_frags(pv, fr);
         accumulate(qp, 1 - h, fr);
       }
-      // dP = dO V^T of this unit
-      f32x16 pacc = {};
+      // dP - D = dO V^T - D of this unit: the products accumulate onto the rows' -D values
+      // (the preprocess stores -D), which saves the subtraction per element
+      float rv[16];
+      read_rows(qt, h, rv);
+      f32x16 pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pacc[r] = rv[r];
 #pragma unroll
       for (int st = 0; st < C::QK_STEPS; ++st) pacc = E::mfma(op[st], bop[st], pacc);
       dp_prev = pacc;
@@ -464,15 +469,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   // the dS wave's last pending unit: the second half of the last tile
   if (dsw) {
     const unsigned char* ql = bufp((total - 1) & 1);
-    float rv[16], pv[16];
-    read_rows(ql, 1, rv);
+    float pv[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const float4 p = *reinterpret_cast<const float4*>(xch + xoff(1, r4));
-      pv[4 * r4 + 0] = p.x * (dp_prev[4 * r4 + 0] - rv[4 * r4 + 0]);
-      pv[4 * r4 + 1] = p.y * (dp_prev[4 * r4 + 1] - rv[4 * r4 + 1]);
-      pv[4 * r4 + 2] = p.z * (dp_prev[4 * r4 + 2] - rv[4 * r4 + 2]);
-      pv[4 * r4 + 3] = p.w * (dp_prev[4 * r4 + 3] - rv[4 * r4 + 3]);
+      pv[4 * r4 + 0] = p.x * dp_prev[4 * r4 + 0];
+      pv[4 * r4 + 1] = p.y * dp_prev[4 * r4 + 1];
+      pv[4 * r4 + 2] = p.z * dp_prev[4 * r4 + 2];
+      pv[4 * r4 + 3] = p.w * dp_prev[4 * r4 + 3];
     }
     frag fr[US];
     to_frags(pv, fr);
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   }
 }
 
-// D_i = sum_d dO_id O_id (float32) and LSE_i * log2(e) (+inf for fully masked rows).  16 threads
+// -D_i = -sum_d dO_id O_id (float32) and LSE_i * log2(e) (+inf for fully masked rows).  16 threads
 // per row, one 16-byte chunk of O and dO each; row r = (b*H + h)*nq + i.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
 #pragma unroll
   for (int off2 = 8; off2 >= 1; off2 >>= 1) acc += __shfl_xor(acc, off2);
   if (c == 0) {
-    delta[row] = acc;
+    delta[row] = -acc;  // stored negated: the dK/dV kernel starts its dP accumulation from it
     // LSE in log2 units; a fully masked row (LSE = -inf) gets +inf so that exp2(s - lse2) = 0
     const float x = lse[row];
     lse2[row] = x == -INFINITY ? INFINITY : x * kLog2e;

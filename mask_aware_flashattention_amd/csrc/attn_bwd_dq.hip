@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   }
   // this row's LSE (log2 units, +inf when fully masked) and D
   const float lse2 = row_ok ? a.lse2[(size_t)bh * a.nq + q_row] : INFINITY;
-  const float dlt = row_ok ? a.delta[(size_t)bh * a.nq + q_row] : 0.0f;
+  const float ndlt = row_ok ? a.delta[(size_t)bh * a.nq + q_row] : 0.0f;  // -D
 
   const int32_t* __restrict__ lst = a.qlist + ((size_t)set * n_qb + qb) * a.list_stride;
   const int last_kb = (a.nk - 1) / C::BN;
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
       for (int e = 0; e < KPL; ++e) {
         const int rb = (t * KPL) / 16, r = (t * KPL) % 16 + e;
         const float p = fast_exp2(fmaf(sacc[rb][r], cexp, -lse2));
-        const float ds = p * (pacc[rb][r] - dlt);
+        const float ds = p * (pacc[rb][r] + ndlt);
         if constexpr (KPL == 1)
           sf[t] = ds;
         else

@@ -96,7 +96,7 @@ struct BwdArgs {
   MaskVecs mask;
   void* dk;
   void* dv;
-  float* delta;   // float32 [B,H,nq]
+  float* delta;   // float32 [B,H,nq]: -D, D_i = sum_d dO_id O_id
   float* lse2;    // float32 [B,H,nq]: LSE * log2(e), +inf on fully masked rows
   const int32_t* kcnt;
   const int32_t* klist;
@@ -118,7 +118,7 @@ struct DqArgs {
   const void* dout;
   MaskVecs mask;
   void* dq;
-  const float* delta;
+  const float* delta;  // -D per row
   const float* lse2;
   const int32_t* qcnt;
   const int32_t* qlist;
