@@ -352,7 +352,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
       if (test) {
         const uint32_t mw = (uint32_t)(mrow >> (32 * h));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pv[r] = ((mw >> perm_index<KPL>(r, 0)) & 1u) ? 0.0f : pv[r];
+        for (int r = 0; r < 16; ++r) pv[r] = select_bit(mw, perm_index<KPL>(r, 0), pv[r], 0u);
       }
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)

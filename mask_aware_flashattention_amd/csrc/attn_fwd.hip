@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t word = mw[rb * 32 + perm_index<KPL>(r, g)];
-          sacc[rb][r] = ((word >> l32) & 1u) ? -INFINITY : sacc[rb][r];
+          sacc[rb][r] = select_bit(word, l32, sacc[rb][r], kNegInfBits);
         }
     }
 

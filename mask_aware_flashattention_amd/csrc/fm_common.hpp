@@ -118,6 +118,14 @@ __device__ inline void pin_value(X& x) {
   }
 }
 
+// x where bit `pos` of `word` is clear, else the float whose bits are `to`: the sign-extended
+// bit is an all-ones / all-zeros select mask for v_bitop3 (two VALU operations in all).
+__device__ inline float select_bit(uint32_t word, uint32_t pos, float x, uint32_t to) {
+  const uint32_t sel = (uint32_t)__builtin_amdgcn_sbfe((int)word, pos, 1);
+  return __builtin_bit_cast(float, __builtin_amdgcn_bitop3_b32(sel, to, __builtin_bit_cast(uint32_t, x), 0xCA));
+}
+constexpr uint32_t kNegInfBits = 0xff800000u;
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Round float to bf16 (round to nearest even) and pack two into a 32-bit word.
