@@ -2,7 +2,7 @@
 
 One step = one pass of the whole path over the workload: flashmask_fwd (block min/max,
 classification, block order, attention forward) then flashmask_bwd (the same at both tile
-shapes, preprocess, dK/dV kernel, dQ kernel); for the context-parallel share the step also
+shapes, dQ kernel, which also writes -D and LSE*log2e per row, then the dK/dV kernel); for the context-parallel share the step also
 starts with flashmask_localize.  ``--workload cp16`` times all 16 ranks of the 128K
 context-parallel share one after another on this GPU (per rank: localize, prune list, forward,
 backward on its 8192 rows against all 131072 keys) beside one global call.  Inputs are seeded synthetic tensors resident in HBM before the

@@ -241,9 +241,10 @@ int32_t flashmask_block_order(const int32_t* cnt, int32_t n, int32_t* order, voi
  * Diagnostic hook for timing the attention kernels alone (a benchmark aid; not needed to use the
  * library).  After this call, flashmask_fwd records fwd_begin / fwd_end and flashmask_bwd
  * records bwd_begin / bwd_end (hipEvent_t passed as void*, created by the caller) on the call's
- * stream immediately before and after its attention kernels (for the backward: before the dK/dV
- * kernel and after the dQ kernel, without the preprocess).  NULL disables a pair.  This is the library's only state:
- * process-wide, not synchronised; set it from the thread that makes the calls.
+ * stream immediately before and after its attention kernels (for the backward: before the dQ
+ * kernel and after the dK/dV kernel, which runs second).  NULL disables a pair.  This is the
+ * library's only state: process-wide, not synchronised; set it from the thread that makes the
+ * calls.
  */
 int32_t flashmask_set_profile_events(void* fwd_begin, void* fwd_end, void* bwd_begin,
                                      void* bwd_end);

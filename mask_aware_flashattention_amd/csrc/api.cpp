@@ -309,14 +309,14 @@ int32_t flashmask_bwd_ex(const fm_layout* l, const void* Q, const void* K, const
   if (e == hipSuccess) e = fm::launch_block_order(kcnt, (int32_t)g.n_kb, korder, hs, sets);
   if (e == hipSuccess) e = fm::launch_block_order(qcnt, (int32_t)gf.n_qb, qorder, hs, sets);
   if (e == hipSuccess) {
-    fm::BwdArgs a{Q,     K,    V,      O,    dO,   LSE,  mv,   dK, dV, delta, lse2, kcnt, klist,
-                  korder, (int32_t)g.n_qb, lay, l->nq, l->nk, scale};
-    e = fm::launch_attn_bwd(l->dtype, a, hs, g_bwd_begin);
+    fm::DqArgs a{Q,    K,     V,     O,     dO,   LSE,  mv,    dQ,   delta, lse2, qcnt, qlist,
+                 qorder, (int32_t)gf.n_kb, lay, l->nq, l->nk, scale};
+    e = fm::launch_attn_dq(l->dtype, a, hs, g_bwd_begin);
   }
   if (e == hipSuccess) {
-    fm::DqArgs a{Q,    K,     V,     dO,    mv,   dQ,   delta, lse2, qcnt, qlist,
-                 qorder, (int32_t)gf.n_kb, lay, l->nq, l->nk, scale};
-    e = fm::launch_attn_dq(l->dtype, a, hs, g_bwd_end);
+    fm::BwdArgs a{Q,     K,    V,      dO,   mv,   dK, dV, delta, lse2, kcnt, klist,
+                  korder, (int32_t)g.n_qb, lay, l->nq, l->nk, scale};
+    e = fm::launch_attn_bwd(l->dtype, a, hs, g_bwd_end);
   }
   return hip_status(e);
 }

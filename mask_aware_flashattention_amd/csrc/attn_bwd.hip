@@ -1,4 +1,4 @@
-// Mask-aware attention backward for gfx950: preprocess and the dK / dV kernel.
+// Mask-aware attention backward for gfx950: the dK / dV kernel.
 //
 // The pages report the backward's speed ("FlashMask-3 ..." zicq.com summary, end-to-end
 // paragraph) but do not describe it; this is the standard recompute-from-LSE backward restricted
@@ -6,7 +6,6 @@
 // partly masked tiles, as the forward; "FlashMask-3 sends each GPU its mask ...",
 // tile-classification paragraph).
 //
-//   K4 bwd_pre:  -D_i = -sum_d dO_id O_id and LSE_i * log2(e) per query row.
 //   K5 dK / dV:  one workgroup of 8 waves per key block of BN = 128 keys: 4 key groups of 32
 //                keys, and per key group a pair of waves on one SIMD that split the work:
 //                  the P wave keeps K rows in registers, computes S = Q K^T, P = exp2(S*scale*
@@ -381,7 +380,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
         accumulate(qp, 1 - h, fr);
       }
       // dP - D = dO V^T - D of this unit: the products accumulate onto the rows' -D values
-      // (the preprocess stores -D), which saves the subtraction per element
+      // (the dQ kernel stores -D), which saves the subtraction per element
       float rv[16];
       read_rows(qt, h, rv);
       f32x16 pacc;
@@ -505,71 +504,27 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   }
 }
 
-// -D_i = -sum_d dO_id O_id (float32) and LSE_i * log2(e) (+inf for fully masked rows).  16 threads
-// per row, one 16-byte chunk of O and dO each; row r = (b*H + h)*nq + i.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o,
-                                                      const T* __restrict__ dout,
-                                                      const float* __restrict__ lse,
-                                                      float* __restrict__ delta,
-                                                      float* __restrict__ lse2, int64_t rows,
-                                                      Layout L, int32_t nq) {
-  constexpr int CH = 16 / (int)sizeof(T);
-  static_assert(D / CH == 16, "16 chunks per row");
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int c = threadIdx.x & 15;
-  if (row >= rows) return;
-  int64_t off = row * D + c * CH;  // contiguous [B][H][nq][d]
-  if (L.qs_r != D || L.qs_h != (int64_t)nq * D || L.qs_b != (int64_t)L.H * nq * D) {
-    const int64_t bh = row / nq, i = row - bh * nq;
-    const int64_t b = bh / L.H, h = bh - b * L.H;
-    off = b * L.qs_b + h * L.qs_h + i * L.qs_r + c * CH;
-  }
-  const uint4 xo = *reinterpret_cast<const uint4*>(o + off);
-  const uint4 xd = *reinterpret_cast<const uint4*>(dout + off);
-  const T* eo = reinterpret_cast<const T*>(&xo);
-  const T* ed = reinterpret_cast<const T*>(&xd);
-  float acc = 0.0f;
-#pragma unroll
-  for (int e = 0; e < CH; ++e) acc = fmaf((float)eo[e], (float)ed[e], acc);
-#pragma unroll
-  for (int off2 = 8; off2 >= 1; off2 >>= 1) acc += __shfl_xor(acc, off2);
-  if (c == 0) {
-    delta[row] = -acc;  // stored negated: the dK/dV kernel starts its dP accumulation from it
-    // LSE in log2 units; a fully masked row (LSE = -inf) gets +inf so that exp2(s - lse2) = 0
-    const float x = lse[row];
-    lse2[row] = x == -INFINITY ? INFINITY : x * kLog2e;
-  }
-}
-
-template <typename T, int D>
-hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin) {
-  const int64_t rows = (int64_t)a.L.B * a.L.H * a.nq;
-  const int pre_grid = (int)((rows + 15) / 16);
-  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, stream,
-                     static_cast<const T*>(a.o), static_cast<const T*>(a.dout), a.lse, a.delta,
-                     a.lse2, rows, a.L, a.nq);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
+hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_end) {
   using C = BwdTile<T, D>;
   const size_t smem = C::SMEM;
   auto kernel = a.L.G > 1 ? &attn_bwd_kernel<T, D, true> : &attn_bwd_kernel<T, D, false>;
-  // The main kernel uses more than 64 KiB of LDS; allow it on the current device.
-  err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  // The kernel uses more than 64 KiB of LDS; allow it on the current device.
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (err != hipSuccess) return err;
   const int64_t n_kb = (a.nk + C::BN - 1) / C::BN;
   const int64_t grid = n_kb * a.L.B * (a.L.H / a.L.G);
-  if (ev_begin) (void)hipEventRecord(ev_begin, stream);
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::NT), smem, stream, a);
-  return hipGetLastError();
+  err = hipGetLastError();
+  if (ev_end) (void)hipEventRecord(ev_end, stream);
+  return err;
 }
 
 }  // namespace
 
-hipError_t launch_attn_bwd(int dtype, const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin) {
-  return dtype == 0 ? run_bwd<bf16, 128>(a, stream, ev_begin) : run_bwd<float, 64>(a, stream, ev_begin);
+hipError_t launch_attn_bwd(int dtype, const BwdArgs& a, hipStream_t stream, hipEvent_t ev_end) {
+  return dtype == 0 ? run_bwd<bf16, 128>(a, stream, ev_end) : run_bwd<float, 64>(a, stream, ev_end);
 }
 
 }  // namespace fm

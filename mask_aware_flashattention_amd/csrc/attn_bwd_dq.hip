@@ -5,8 +5,10 @@
 // block per workgroup, walking the same list of key tiles the forward walks (fully masked tiles
 // skipped, the row test only in partly masked tiles; "FlashMask-3 sends each GPU its mask ...",
 // tile-classification paragraph), recomputing P from the saved LSE and dP from dO and V.
-// dK and dV come from the key-stationary kernel in attn_bwd.hip; splitting the two products
-// this way needs no float32 atomics and gives a deterministic dQ.
+// dK and dV come from the key-stationary kernel in attn_bwd.hip, launched after this one;
+// splitting the two products this way needs no float32 atomics and gives a deterministic dQ.
+// Before its tile loop each workgroup reads its rows of O once and writes, per row,
+// -D = -sum_d dO_id O_id and LSE * log2(e) for the dK / dV kernel (no separate pass).
 //
 // Layout (the forward's, with dP added): one workgroup = 4 waves = 128 query rows against key
 // tiles of 64; each wave holds its 32 rows of Q and dO in registers as the B operands of
@@ -96,13 +98,22 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   const int q_row = q0w + l32;          // this lane's query row
   const bool row_ok = q_row < a.nq;
   const int cnt = a.qcnt[(size_t)set * n_qb + qb];
+  // Per row, for this kernel and the dK/dV kernel that runs after it: LSE * log2(e) (+inf on a
+  // fully masked row, so that exp2(s - lse2) = 0) and -D, D = sum_d dO_id O_id.
+  const size_t row_idx = (size_t)bh * a.nq + q_row;
+  const float lse_row = row_ok ? a.lse[row_idx] : -INFINITY;
+  const float lse2 = lse_row == -INFINITY ? INFINITY : lse_row * kLog2e;
   if (cnt == 0) {
     // No listed tile: the block's rows are fully masked, so dQ = 0 (each lane clears half of
-    // its row, 128 bytes).
+    // its row, 128 bytes) and the rows' D is never used.
     if (row_ok) {
       uint4* p = reinterpret_cast<uint4*>(dQp + (size_t)q_row * a.L.qs_r + g * (D / 2));
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (g == 0) {
+        a.delta[row_idx] = 0.0f;
+        a.lse2[row_idx] = lse2;
+      }
     }
     return;
   }
@@ -121,9 +132,30 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
       dof[s] = __builtin_bit_cast(frag, buf_load4(dobuf, off, 0));
     }
   }
-  // this row's LSE (log2 units, +inf when fully masked) and D
-  const float lse2 = row_ok ? a.lse2[(size_t)bh * a.nq + q_row] : INFINITY;
-  const float ndlt = row_ok ? a.delta[(size_t)bh * a.nq + q_row] : 0.0f;  // -D
+  // D of this row from its O and dO: lanes l and l ^ 32 hold the two halves of the row.
+  float ndlt;  // -D
+  {
+    const T* __restrict__ Op = static_cast<const T*>(a.o) + qbase;
+    const buf_rsrc obuf = make_buf(Op, (uint32_t)(a.nq - 1) * qrs + C::ROW_BYTES);
+    float part = 0.0f;
+#pragma unroll
+    for (int s = 0; s < C::QK_STEPS; ++s) {
+      const uint32_t off = (uint32_t)q_row * qrs + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
+      if constexpr (KPL == 8) {
+        const frag of = __builtin_bit_cast(frag, buf_load16(obuf, off, 0));
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) part = fmaf((float)dof[s][e], (float)of[e], part);
+      } else {
+        const float of = __builtin_bit_cast(float, buf_load4(obuf, off, 0));
+        part = fmaf(dof[s], of, part);
+      }
+    }
+    ndlt = -pair_sum32(part);
+    if (row_ok && g == 0) {
+      a.delta[row_idx] = ndlt;
+      a.lse2[row_idx] = lse2;
+    }
+  }
 
   const int32_t* __restrict__ lst = a.qlist + ((size_t)set * n_qb + qb) * a.list_stride;
   const int last_kb = (a.nk - 1) / C::BN;
@@ -299,23 +331,22 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
 }
 
 template <typename T, int D>
-hipError_t run_dq(const DqArgs& a, hipStream_t stream, hipEvent_t ev_end) {
+hipError_t run_dq(const DqArgs& a, hipStream_t stream, hipEvent_t ev_begin) {
   using C = DqTile<T, D>;
   const int64_t n_qb = (a.nq + C::BM - 1) / C::BM;
   const int64_t grid = n_qb * a.L.B * a.L.H;
+  if (ev_begin) (void)hipEventRecord(ev_begin, stream);
   hipLaunchKernelGGL((attn_dq_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
-  const hipError_t err = hipGetLastError();
-  if (ev_end) (void)hipEventRecord(ev_end, stream);
-  return err;
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_dq(int dtype, const DqArgs& a, hipStream_t stream, hipEvent_t ev_end) {
+hipError_t launch_attn_dq(int dtype, const DqArgs& a, hipStream_t stream, hipEvent_t ev_begin) {
   // The lists were built at the forward's tile shape; this kernel walks them at the same shape.
   const TileShape t = tile_shape(dtype);
   if (t.bm_fwd != DqTile<bf16, 128>::BM || t.bn_fwd != DqTile<bf16, 128>::BN) return hipErrorInvalidValue;
-  return dtype == 0 ? run_dq<bf16, 128>(a, stream, ev_end) : run_dq<float, 64>(a, stream, ev_end);
+  return dtype == 0 ? run_dq<bf16, 128>(a, stream, ev_begin) : run_dq<float, 64>(a, stream, ev_begin);
 }
 
 }  // namespace fm

@@ -85,8 +85,10 @@ struct FwdArgs {
 hipError_t launch_attn_fwd(int dtype, const FwdArgs& a, hipStream_t stream, hipEvent_t ev_begin,
                            hipEvent_t ev_end);
 
-// Backward, key-stationary part: D = rowsum(dO * O) and LSE * log2(e) (bwd_pre), then dK, dV.
-struct BwdArgs {
+// Backward, query-stationary part, run first: dQ over the forward's tile lists; it also writes,
+// per row, -D (D_i = sum_d dO_id O_id) and LSE * log2(e) (+inf on fully masked rows) for the
+// dK/dV kernel.
+struct DqArgs {
   const void* q;
   const void* k;
   const void* v;
@@ -94,32 +96,9 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   MaskVecs mask;
-  void* dk;
-  void* dv;
-  float* delta;   // float32 [B,H,nq]: -D, D_i = sum_d dO_id O_id
-  float* lse2;    // float32 [B,H,nq]: LSE * log2(e), +inf on fully masked rows
-  const int32_t* kcnt;
-  const int32_t* klist;
-  const int32_t* order;  // key blocks, longest list first
-  int32_t list_stride;  // n_qb at the backward tile shape
-  Layout L;
-  int32_t nq, nk;
-  float scale;
-};
-// Runs bwd_pre and the dK/dV kernel; ev_begin (may be null) is recorded before the dK/dV kernel.
-hipError_t launch_attn_bwd(int dtype, const BwdArgs& a, hipStream_t stream, hipEvent_t ev_begin);
-
-// Backward, query-stationary part: dQ over the forward's tile lists (needs delta and lse2 from
-// launch_attn_bwd on the same stream).
-struct DqArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* dout;
-  MaskVecs mask;
   void* dq;
-  const float* delta;  // -D per row
-  const float* lse2;
+  float* delta;  // float32 [B,H,nq]: -D
+  float* lse2;   // float32 [B,H,nq]
   const int32_t* qcnt;
   const int32_t* qlist;
   const int32_t* order;  // query blocks, longest list first
@@ -128,8 +107,31 @@ struct DqArgs {
   int32_t nq, nk;
   float scale;
 };
-// ev_end (may be null) is recorded after the dQ kernel.
-hipError_t launch_attn_dq(int dtype, const DqArgs& a, hipStream_t stream, hipEvent_t ev_end);
+// ev_begin (may be null) is recorded before the dQ kernel.
+hipError_t launch_attn_dq(int dtype, const DqArgs& a, hipStream_t stream, hipEvent_t ev_begin);
+
+// Backward, key-stationary part: dK, dV (needs delta and lse2 from launch_attn_dq on the same
+// stream).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  MaskVecs mask;
+  void* dk;
+  void* dv;
+  const float* delta;  // -D per row
+  const float* lse2;   // LSE * log2(e) per row
+  const int32_t* kcnt;
+  const int32_t* klist;
+  const int32_t* order;  // key blocks, longest list first
+  int32_t list_stride;  // n_qb at the backward tile shape
+  Layout L;
+  int32_t nq, nk;
+  float scale;
+};
+// ev_end (may be null) is recorded after the dK/dV kernel.
+hipError_t launch_attn_bwd(int dtype, const BwdArgs& a, hipStream_t stream, hipEvent_t ev_end);
 
 // Tile shapes of the attention kernels (the shapes tiles are classified at).
 struct TileShape {
