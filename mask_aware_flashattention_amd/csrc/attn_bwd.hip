@@ -395,10 +395,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   };
 
   // ---- the walk over the key block's query tiles ---------------------------------------------
-  // Tile t sits in buffer t % 2.  The barrier of a tile's second unit also publishes tile t+1,
-  // committed just before it into the buffer tile t-1 used (after the first unit's barrier of
-  // tile t no wave reads tile t-1: the dS wave finished its lagging unit of tile t-1 before that
-  // barrier); tile t+2 is then loaded.
+  // Tile t sits in buffer t % 2.  Right after the barrier of tile t's first unit, tile t+1 is
+  // written from registers into the buffer tile t-1 used (after that barrier no wave reads tile
+  // t-1: the dS wave finished its lagging unit of tile t-1 before it) and tile t+2 is loaded into
+  // registers; the barrier of the second unit publishes tile t+1.  The LDS writes so have a whole
+  // unit to complete before a barrier waits on them.
   // The walk is written out once per role (same barriers in the same order), so that neither
   // role's loop carries the other's registers.
   using H0 = std::integral_constant<int, 0>;
@@ -435,20 +436,20 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
         }
       }
       const unsigned char* qt = bufp(b);
-      step(role, qt, H0{}, test, mrow, [] { __syncthreads(); }, op, dp_prev, true, qt, 1,
-           bufp(b ^ 1), t > 0);
       const bool more = t + 1 < total;
-      step(role, qt, H1{}, test, mrow, [&] {
-        if (more) {
-          wait_vmem();       // tile t+1 is in this wave's registers
-          commit_tile(b ^ 1);
-        }
+      step(role, qt, H0{}, test, mrow, [&] {
         __syncthreads();
-        if (t + 2 < total) {
-          load_tile(ahead.gi, entry_of(ahead));
-          advance(ahead);
+        if (more) {
+          wait_vmem();         // tile t+1 is in this wave's registers
+          commit_tile(b ^ 1);  // published by the next barrier
+          if (t + 2 < total) {
+            load_tile(ahead.gi, entry_of(ahead));
+            advance(ahead);
+          }
         }
-      }, op, dp_prev, more, bufp(b ^ 1), 0, qt, true);
+      }, op, dp_prev, true, qt, 1, bufp(b ^ 1), t > 0);
+      step(role, qt, H1{}, test, mrow, [] { __syncthreads(); }, op, dp_prev, more, bufp(b ^ 1), 0,
+           qt, true);
       if (more) {
         advance(cur);
         entry = entry_of(cur);
