@@ -45,7 +45,6 @@ struct BwdTile {
   static constexpr int TILE_BYTES = BM * ROW_BYTES;
   static constexpr int BUF_BYTES = 2 * TILE_BYTES + 2 * BM * (int)sizeof(float);  // Q|dO|LSE2|D
   static constexpr int XCH_BYTES = 4 * 16 * 64 * (int)sizeof(float);  // one unit's P, 4 groups
-  static constexpr int SMEM = 2 * BUF_BYTES + 2 * XCH_BYTES;
   static_assert(CPR == 16, "tile loads assume 256-byte rows");
   static_assert(TILE_BYTES == 16 * 1024, "16 blocks of 1 KiB per tile");
 };
@@ -63,12 +62,24 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   using frag = typename E::frag;
   constexpr int KPL = C::KPL, KSTEP = C::KSTEP, US = C::US;
 
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  auto bufp = [&](int b) -> unsigned char* { return smem + b * C::BUF_BYTES; };
-  auto rowsp = [&](int b) -> float* {
-    return reinterpret_cast<float*>(smem + b * C::BUF_BYTES + 2 * C::TILE_BYTES);
+  // Three tile buffers, Q|dO|LSE2|D each, as separate arrays: the compiler then sees that the
+  // loads straight into one buffer never alias reads of another and adds no waits for them.
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[C::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[C::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds2[C::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) float xch[2 * C::XCH_BYTES / sizeof(float)];  // [2 units][4 groups][4][64][4]
+  auto bufp = [&](auto bc) -> unsigned char* {
+    constexpr int bi = decltype(bc)::value;
+    if constexpr (bi == 0)
+      return lds0;
+    else if constexpr (bi == 1)
+      return lds1;
+    else
+      return lds2;
   };
-  float* xch = reinterpret_cast<float*>(smem + 2 * C::BUF_BYTES);  // [2 units][4 groups][4][64][4]
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -200,7 +211,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
       if (u.gi < G) head_list(u);
     }
   };
-  auto entry_of = [&](const Cursor& u) { return __builtin_amdgcn_readfirstlane(u.l[u.i]); };
+  auto entry_of = [&](const Cursor& u) { return load_uniform(u.l, u.i); };
   // This lane's key's mask values for the tile's head; reloaded only when the head's mask set
   // changes (never with one set per batch).
   MaskRegs mk = {0, 0, 0, 0};  // past the last key every row is masked
@@ -224,15 +235,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   // A tile's 64 rows of Q, then of dO, are 32 blocks of 1 KiB; wave w moves blocks 4w..4w+3
   // (waves 0-3 Q, 4-7 dO), lane l the 16-byte slot l of a block: row 4j + l/16 of its tensor,
   // physical chunk l%16, which holds logical chunk (l%16) ^ swz_row(row).  Rows past nq read as
-  // zeros.  Waves 0 and 1 also move the tile's LSE2 and D rows.  The loads go to registers first
-  // (load_tile) and are written to LDS a tile later (commit_tile), so no LDS read ever waits on
-  // a load in flight.
-  uint4 stg[4];
-  float strow = 0.0f;
+  // zeros.  Waves 0 and 1 also move the tile's LSE2 and D rows.  The loads go straight into LDS
+  // (no registers, no LDS writes by the waves); kTileLoads[wave < 2] of them per wave and tile.
   // The buffers span all G heads, so rows past nq of one head are another head's rows: their
   // offsets are moved to the buffer's end, where loads return zeros (dO = 0 and D = 0 make such a
   // row contribute nothing).
-  auto load_tile = [&](int gi, int entry) {
+  auto load_tile = [&](int gi, int entry, auto bc) {
+    unsigned char* t = bufp(bc);
     const int q0 = (entry >> 1) * C::BM;
     const uint32_t tile_base = (uint32_t)gi * qhs + (uint32_t)q0 * qrs;
     const buf_rsrc src = wv < 4 ? qbuf : dobuf;
@@ -242,20 +251,24 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
       const uint32_t voff = !GQ || q0 + row < a.nq
                                 ? (uint32_t)row * qrs + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16)
                                 : q_span - tile_base;
-      stg[i] = buf_load16(src, voff, tile_base);
+      buf_load_lds<16>(src, t + (4 * wv + i) * 1024, voff, tile_base);
     }
     if (wv < 2) {
       const uint32_t roff = ((uint32_t)gi * a.nq + (uint32_t)q0) * sizeof(float);
       const uint32_t r_span = (uint32_t)G * a.nq * sizeof(float);
       const uint32_t loff = !GQ || q0 + lane < a.nq ? (uint32_t)lane * sizeof(float) : r_span - roff;
-      strow = __builtin_bit_cast(float, buf_load4(wv == 0 ? lbuf : dlbuf, loff, roff));
+      buf_load_lds<4>(wv == 0 ? lbuf : dlbuf, t + 2 * C::TILE_BYTES + wv * C::BM * sizeof(float), loff,
+                      roff);
     }
   };
-  auto commit_tile = [&](int b) {
-    unsigned char* t = bufp(b);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(t + (4 * wv + i) * 1024 + lane * 16) = stg[i];
-    if (wv < 2) rowsp(b)[wv * C::BM + lane] = strow;
+  // Wait until this wave's loads of the older of the (one or two) tiles in flight have landed.
+  auto wait_older_tile = [&](bool newer_in_flight) {
+    if (!newer_in_flight)
+      wait_vmem();
+    else if (wv < 2)
+      wait_vmem_n<5>();
+    else
+      wait_vmem_n<4>();
   };
 
   // Row mask of this lane's key over a tile's BM query rows starting at q0 (bit i = row q0 + i
@@ -395,38 +408,40 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   };
 
   // ---- the walk over the key block's query tiles ---------------------------------------------
-  // Tile t sits in buffer t % 2.  Right after the barrier of tile t's first unit, tile t+1 is
-  // written from registers into the buffer tile t-1 used (after that barrier no wave reads tile
-  // t-1: the dS wave finished its lagging unit of tile t-1 before it) and tile t+2 is loaded into
-  // registers; the barrier of the second unit publishes tile t+1.  The LDS writes so have a whole
-  // unit to complete before a barrier waits on them.
+  // Tile t sits in buffer t % 3.  Right after the barrier of tile t's first unit, the loads of
+  // tile t+2 into the buffer tile t-1 used are issued (after that barrier no wave reads tile t-1:
+  // the dS wave finished its lagging unit of tile t-1 before it); before the barrier of tile t's
+  // second unit each wave waits for its loads of tile t+1 (issued a tile earlier), and the
+  // barrier publishes that tile.  A load so has three units to land.
   // The walk is written out once per role (same barriers in the same order), so that neither
   // role's loop carries the other's registers.
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
   {
-    load_tile(first.gi, entry_of(first));
-    wait_vmem();
-    commit_tile(0);
-    __syncthreads();
+    load_tile(first.gi, entry_of(first), I0{});
     if (total > 1) {
       Cursor second = first;
       advance(second);
-      load_tile(second.gi, entry_of(second));
+      load_tile(second.gi, entry_of(second), I1{});
     }
+    wait_older_tile(total > 1);
+    __syncthreads();
   }
   f32x16 dp_prev = {};  // dS wave: dP of the pending unit
   auto walk = [&](auto role) {
     Cursor cur = first;        // the tile being walked
-    Cursor ahead = first;      // the tile two ahead, whose rows are loaded at the tile's end
+    Cursor ahead = first;      // the tile two ahead, loaded during this one
     advance(ahead);
     if (total > 1) advance(ahead);
     int entry = entry_of(cur);
     frag op[C::QK_STEPS];
-    read_ops(bufp(0), 0, op);
-    // tile t in buffer bc (a compile-time constant, so LDS offsets fold into the instructions)
+    read_ops(bufp(I0{}), 0, op);
+    // tile t in buffer bc = t % 3 (a compile-time constant, so LDS offsets fold into the
+    // instructions); tile t+1 is in buffer (bc+1) % 3, tile t-1 was in (bc+2) % 3
     auto tile = [&](const int t, auto bc) {
-      constexpr int b = decltype(bc)::value;
+      constexpr int bi = decltype(bc)::value;
+      using BNext = std::integral_constant<int, (bi + 1) % 3>;
+      using BPrev = std::integral_constant<int, (bi + 2) % 3>;
       const bool test = (entry & 1) || ragged_block;
       uint64_t mrow = 0ull;  // the row test belongs to the P wave only
       if constexpr (!decltype(role)::value) {
@@ -435,32 +450,33 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
           mrow = tile_row_mask((entry >> 1) * C::BM);
         }
       }
-      const unsigned char* qt = bufp(b);
+      const unsigned char* qt = bufp(bc);
       const bool more = t + 1 < total;
+      const bool more2 = t + 2 < total;
       step(role, qt, H0{}, test, mrow, [&] {
-        __syncthreads();
-        if (more) {
-          wait_vmem();         // tile t+1 is in this wave's registers
-          commit_tile(b ^ 1);  // published by the next barrier
-          if (t + 2 < total) {
-            load_tile(ahead.gi, entry_of(ahead));
-            advance(ahead);
-          }
+        lds_barrier();
+        if (more2) {  // into tile t-1's buffer: no wave reads it after this barrier
+          load_tile(ahead.gi, entry_of(ahead), BPrev{});
+          advance(ahead);
         }
-      }, op, dp_prev, true, qt, 1, bufp(b ^ 1), t > 0);
-      step(role, qt, H1{}, test, mrow, [] { __syncthreads(); }, op, dp_prev, more, bufp(b ^ 1), 0,
-           qt, true);
+      }, op, dp_prev, true, qt, 1, bufp(BPrev{}), t > 0);
+      step(role, qt, H1{}, test, mrow, [&] {
+        if (more) wait_older_tile(more2);  // this wave's part of tile t+1 has landed ...
+        lds_barrier();                     // ... and everyone's
+      }, op, dp_prev, more, bufp(BNext{}), 0, qt, true);
       if (more) {
         advance(cur);
         entry = entry_of(cur);
       }
     };
     int t = 0;
-    for (; t + 1 < total; t += 2) {
-      tile(t, std::integral_constant<int, 0>{});
-      tile(t + 1, std::integral_constant<int, 1>{});
+    for (; t + 2 < total; t += 3) {
+      tile(t, I0{});
+      tile(t + 1, I1{});
+      tile(t + 2, I2{});
     }
-    if (t < total) tile(t, std::integral_constant<int, 0>{});
+    if (t < total) tile(t, I0{});
+    if (t + 1 < total) tile(t + 1, I1{});
   };
   if (dsw)
     walk(std::true_type{});
@@ -468,7 +484,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
     walk(std::false_type{});
   // the dS wave's last pending unit: the second half of the last tile
   if (dsw) {
-    const unsigned char* ql = bufp((total - 1) & 1);
+    const int lb = (total - 1) % 3;
+    const unsigned char* ql = lb == 0 ? lds0 : (lb == 1 ? lds1 : lds2);
     float pv[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -508,16 +525,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
 template <typename T, int D>
 hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_end) {
   using C = BwdTile<T, D>;
-  const size_t smem = C::SMEM;
   auto kernel = a.L.G > 1 ? &attn_bwd_kernel<T, D, true> : &attn_bwd_kernel<T, D, false>;
-  // The kernel uses more than 64 KiB of LDS; allow it on the current device.
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (err != hipSuccess) return err;
   const int64_t n_kb = (a.nk + C::BN - 1) / C::BN;
   const int64_t grid = n_kb * a.L.B * (a.L.H / a.L.G);
-  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::NT), smem, stream, a);
-  err = hipGetLastError();
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
+  hipError_t err = hipGetLastError();
   if (ev_end) (void)hipEventRecord(ev_end, stream);
   return err;
 }

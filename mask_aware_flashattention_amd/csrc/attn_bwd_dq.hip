@@ -229,13 +229,13 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) dq_acc[db] = f32x16{};
 
-  int entry = cnt > 0 ? __builtin_amdgcn_readfirstlane(lst[0]) : 0;
+  int entry = cnt > 0 ? load_uniform(lst, 0) : 0;
 
   auto body = [&](const int it, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const int kb = entry >> 1;
     const bool test = (entry & 1) || (kb == last_kb && ragged);
-    const int next = it + 1 < cnt ? __builtin_amdgcn_readfirstlane(lst[it + 1]) : 0;
+    const int next = it + 1 < cnt ? load_uniform(lst, it + 1) : 0;
     wait_vmem();      // this wave's loads of tile `it` have landed in LDS
     __syncthreads();  // ... everyone's, and the mask words
     if (it + 1 < cnt) issue_tile(next, std::integral_constant<int, buf ^ 1>{});

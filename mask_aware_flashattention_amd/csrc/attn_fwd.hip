@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   float m_run = -INFINITY;  // reference max (scale*log2(e) units) for this lane's row
   float l_run = 0.0f;       // this lane's share of the running sum (its 32 keys of each tile)
 
-  int entry = __builtin_amdgcn_readfirstlane(lst[0]);
+  int entry = load_uniform(lst, 0);
 
   auto body = [&](const int it, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     // The last tile stages its own rows again into the free buffer, which is never read: the
     // staging then needs no branch inside the products.
     const bool has_next = it + 1 < cnt;
-    const int next = has_next ? __builtin_amdgcn_readfirstlane(lst[it + 1]) : entry;
+    const int next = has_next ? load_uniform(lst, it + 1) : entry;
     const bool next_test = has_next && is_test(next);
     wait_vmem();      // this wave's loads of tile `it` have landed in LDS
     __syncthreads();  // ... everyone's, and the mask words; the other buffer is free

@@ -211,6 +211,31 @@ __device__ inline void buf_load_lds(buf_rsrc r, void* lds_base, uint32_t voff, u
 // Wait until this wave's outstanding vector-memory operations (including loads into LDS) are
 // complete: s_waitcnt vmcnt(0), other counters left alone.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Read a value that is the same for the whole wave and constant while the kernel runs (written
+// by an earlier launch) through the scalar path: s_load, counted by lgkmcnt, so the read never
+// has to wait for vector loads in flight (a vector load would need s_waitcnt vmcnt(0)).
+__device__ inline int32_t load_uniform(const int32_t* p, int i) {
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  return ((const_i32*)p)[i];
+}
+// Workgroup barrier for data exchanged through LDS only: waits for this wave's LDS (and scalar)
+// operations, lgkmcnt(0), but not for its vector-memory loads; __syncthreads() also waits
+// vmcnt(0), which would stall on loads still in flight for a later tile.  Loads straight into
+// LDS are covered by the caller's own vmcnt wait.  The empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// s_waitcnt vmcnt(N): wait until at most N of this wave's vector-memory operations are in
+// flight (they complete in issue order).
+template <int N>
+__device__ inline void wait_vmem_n() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
 
 // ---- LDS transpose read (gfx950 ds_read_b64_tr_b16) ------------------------------------------
 // Within each block of 16 lanes, lane i receives element i%4 of the four 16-bit elements that
