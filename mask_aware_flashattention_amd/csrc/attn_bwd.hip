@@ -43,7 +43,10 @@ struct BwdTile {
   static constexpr int QK_STEPS = D / KSTEP;
   static constexpr int US = 32 / KSTEP;  // k-steps over a unit's 32 queries
   static constexpr int TILE_BYTES = BM * ROW_BYTES;
-  static constexpr int BUF_BYTES = 2 * TILE_BYTES + 2 * BM * (int)sizeof(float);  // Q|dO|LSE2|D
+  // Q | dO | rows: LSE2 and D of the tile's rows in 8 slots of 64 floats, slot w filled by
+  // wave w (16 rows in its first 16 floats; LSE2 in slots 0-3, D in 4-7)
+  static constexpr int ROWS_BYTES = 8 * 64 * (int)sizeof(float);
+  static constexpr int BUF_BYTES = 2 * TILE_BYTES + ROWS_BYTES;
   static constexpr int XCH_BYTES = 4 * 16 * 64 * (int)sizeof(float);  // one unit's P, 4 groups
   static_assert(CPR == 16, "tile loads assume 256-byte rows");
   static_assert(TILE_BYTES == 16 * 1024, "16 blocks of 1 KiB per tile");
@@ -235,8 +238,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   // A tile's 64 rows of Q, then of dO, are 32 blocks of 1 KiB; wave w moves blocks 4w..4w+3
   // (waves 0-3 Q, 4-7 dO), lane l the 16-byte slot l of a block: row 4j + l/16 of its tensor,
   // physical chunk l%16, which holds logical chunk (l%16) ^ swz_row(row).  Rows past nq read as
-  // zeros.  Waves 0 and 1 also move the tile's LSE2 and D rows.  The loads go straight into LDS
-  // (no registers, no LDS writes by the waves); kTileLoads[wave < 2] of them per wave and tile.
+  // zeros.  Each wave also moves 16 of the tile's LSE2 (waves 0-3) or D (waves 4-7) values, in
+  // lanes 0-15 of its row slot (lanes 16-63 read out of range and write zeros into the rest of the
+  // slot).  The loads go straight into LDS (no registers, no LDS writes by the waves): five per
+  // wave and tile, the same for every wave, so one vmcnt value covers a tile.
   // The buffers span all G heads, so rows past nq of one head are another head's rows: their
   // offsets are moved to the buffer's end, where loads return zeros (dO = 0 and D = 0 make such a
   // row contribute nothing).
@@ -253,23 +258,18 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
                                 : q_span - tile_base;
       buf_load_lds<16>(src, t + (4 * wv + i) * 1024, voff, tile_base);
     }
-    if (wv < 2) {
+    {
+      const int r = 16 * (wv & 3) + lane;  // tile row of this lane (lanes below 16)
       const uint32_t roff = ((uint32_t)gi * a.nq + (uint32_t)q0) * sizeof(float);
       const uint32_t r_span = (uint32_t)G * a.nq * sizeof(float);
-      const uint32_t loff = !GQ || q0 + lane < a.nq ? (uint32_t)lane * sizeof(float) : r_span - roff;
-      buf_load_lds<4>(wv == 0 ? lbuf : dlbuf, t + 2 * C::TILE_BYTES + wv * C::BM * sizeof(float), loff,
-                      roff);
+      const uint32_t loff = lane < 16 && (!GQ || q0 + r < a.nq) ? (uint32_t)r * sizeof(float) : r_span - roff;
+      buf_load_lds<4>(wv < 4 ? lbuf : dlbuf, t + 2 * C::TILE_BYTES + wv * 64 * sizeof(float), loff, roff);
     }
   };
-  // Wait until this wave's loads of the older of the (one or two) tiles in flight have landed.
-  auto wait_older_tile = [&](bool newer_in_flight) {
-    if (!newer_in_flight)
-      wait_vmem();
-    else if (wv < 2)
-      wait_vmem_n<5>();
-    else
-      wait_vmem_n<4>();
-  };
+  // Every tile step issues exactly one tile's five loads (near the end of the walk a real tile is
+  // loaded again into a buffer nothing reads any more), so one wait without a branch, vmcnt(5),
+  // leaves only the newest tile's loads in flight; a wait under a branch would make the
+  // compiler's own wait tracking assume the no-wait path and add vmcnt(0) before later reads.
 
   // Row mask of this lane's key over a tile's BM query rows starting at q0 (bit i = row q0 + i
   // masked), pre-shifted by g*KPL so that bit h*32 + perm_index(r, 0) belongs to register r of
@@ -299,18 +299,22 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   // Rows of a unit's LSE2 (P wave) or D (dS wave) for the 16 queries this lane holds: runs of
   // KPL consecutive rows h*32 + (r/KPL)*2*KPL + g*KPL + 0..KPL-1.
   auto read_rows = [&](const unsigned char* qt, int h, float* rv) {
-    const float* rows = reinterpret_cast<const float*>(qt + 2 * C::TILE_BYTES) + (dsw ? C::BM : 0);
+    // row q of the tile is float (q / 16) * 64 + q % 16 of the LSE2 or D half of the slots
+    const float* rows = reinterpret_cast<const float*>(qt + 2 * C::TILE_BYTES) + (dsw ? 4 * 64 : 0);
     if constexpr (KPL == 8) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float4 x0 = *reinterpret_cast<const float4*>(rows + h * 32 + 16 * j + 8 * g);
-        const float4 x1 = *reinterpret_cast<const float4*>(rows + h * 32 + 16 * j + 8 * g + 4);
+        const float4 x0 = *reinterpret_cast<const float4*>(rows + (2 * h + j) * 64 + 8 * g);
+        const float4 x1 = *reinterpret_cast<const float4*>(rows + (2 * h + j) * 64 + 8 * g + 4);
         rv[8 * j + 0] = x0.x; rv[8 * j + 1] = x0.y; rv[8 * j + 2] = x0.z; rv[8 * j + 3] = x0.w;
         rv[8 * j + 4] = x1.x; rv[8 * j + 5] = x1.y; rv[8 * j + 6] = x1.z; rv[8 * j + 7] = x1.w;
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) rv[r] = rows[h * 32 + perm_index<KPL>(r, g)];
+      for (int r = 0; r < 16; ++r) {
+        const int q = h * 32 + perm_index<KPL>(r, g);
+        rv[r] = rows[(q >> 4) * 64 + (q & 15)];
+      }
     }
   };
   // operand fragments of P or dS: k-step u covers queries h*32 + u*KSTEP + g*KPL + e =
@@ -410,22 +414,21 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   // ---- the walk over the key block's query tiles ---------------------------------------------
   // Tile t sits in buffer t % 3.  Right after the barrier of tile t's first unit, the loads of
   // tile t+2 into the buffer tile t-1 used are issued (after that barrier no wave reads tile t-1:
-  // the dS wave finished its lagging unit of tile t-1 before it); before the barrier of tile t's
-  // second unit each wave waits for its loads of tile t+1 (issued a tile earlier), and the
-  // barrier publishes that tile.  A load so has three units to land.
+  // the dS wave finished its lagging unit of tile t-1 before it; the last two tiles load a tile
+  // again instead); before the barrier of tile t's second unit each wave waits for its loads of
+  // tile t+1 (issued a tile earlier), and the barrier publishes that tile.  A load so has three
+  // units to land.
   // The walk is written out once per role (same barriers in the same order), so that neither
   // role's loop carries the other's registers.
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
   {
     load_tile(first.gi, entry_of(first), I0{});
-    if (total > 1) {
-      Cursor second = first;
-      advance(second);
-      load_tile(second.gi, entry_of(second), I1{});
-    }
-    wait_older_tile(total > 1);
-    __syncthreads();
+    Cursor second = first;
+    if (total > 1) advance(second);
+    load_tile(second.gi, entry_of(second), I1{});  // tile 1, or tile 0 again (never read)
+    wait_vmem_n<5>();                              // tile 0 has landed
+    lds_barrier();
   }
   f32x16 dp_prev = {};  // dS wave: dP of the pending unit
   auto walk = [&](auto role) {
@@ -455,14 +458,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
       const bool more2 = t + 2 < total;
       step(role, qt, H0{}, test, mrow, [&] {
         lds_barrier();
-        if (more2) {  // into tile t-1's buffer: no wave reads it after this barrier
-          load_tile(ahead.gi, entry_of(ahead), BPrev{});
-          advance(ahead);
-        }
+        // tile t+2 (or tile t again, never read) into tile t-1's buffer: no wave reads that
+        // buffer after this barrier
+        const Cursor& src = more2 ? ahead : cur;
+        load_tile(src.gi, entry_of(src), BPrev{});
+        if (more2) advance(ahead);
       }, op, dp_prev, true, qt, 1, bufp(BPrev{}), t > 0);
       step(role, qt, H1{}, test, mrow, [&] {
-        if (more) wait_older_tile(more2);  // this wave's part of tile t+1 has landed ...
-        lds_barrier();                     // ... and everyone's
+        wait_vmem_n<5>();  // this wave's part of tile t+1 has landed ...
+        lds_barrier();     // ... and everyone's
       }, op, dp_prev, more, bufp(BNext{}), 0, qt, true);
       if (more) {
         advance(cur);
@@ -482,6 +486,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
     walk(std::true_type{});
   else
     walk(std::false_type{});
+  // The last two tile steps loaded a tile again into a free buffer; those loads must land before
+  // the workgroup ends and its LDS is handed to another.
+  wait_vmem();
   // the dS wave's last pending unit: the second half of the last tile
   if (dsw) {
     const int lb = (total - 1) % 3;
