@@ -49,12 +49,13 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
   using frag = typename E::frag;
   constexpr int KPL = C::KPL, KSTEP = C::KSTEP;
 
-  // LDS: two buffers [K | V | mask words].  They are separate arrays so that the compiler can
-  // tell that loads into one buffer never overlap reads of the other, and adds no wait on the
-  // loads in flight before those reads.
-  constexpr int BUF_BYTES = 2 * C::TILE_BYTES + C::MW_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char lds0[BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char lds1[BUF_BYTES];
+  // LDS: two tile buffers [K | V] and two arrays of mask words.  They are separate arrays so
+  // that the compiler can tell that loads into one buffer never overlap reads of the other or
+  // the mask words, and adds no wait on the loads in flight before those accesses.
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[2 * C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[2 * C::TILE_BYTES];
+  __shared__ uint32_t mw0[C::MW_BYTES / 4];
+  __shared__ uint32_t mw1[C::MW_BYTES / 4];
   auto bufp = [&](auto bc) -> unsigned char* {
     if constexpr (decltype(bc)::value == 0)
       return lds0;
@@ -62,7 +63,10 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
       return lds1;
   };
   auto mwp = [&](auto bc) -> uint32_t* {
-    return reinterpret_cast<uint32_t*>(bufp(bc) + 2 * C::TILE_BYTES);
+    if constexpr (decltype(bc)::value == 0)
+      return mw0;
+    else
+      return mw1;
   };
 
   const int tid = threadIdx.x;
@@ -192,8 +196,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
 
   // Stage key tile `entry` into buffer `bufc`: K then V, 16 blocks of 1 KiB each, wave w fills
   // blocks 4w..4w+3 (lane l: row 4j + l/16, physical chunk l%16 = logical chunk
-  // (l%16) ^ swz_row(row)); keys past nk read as zeros.  In partly masked tiles thread tid
-  // also writes the row mask of key tid%64 for wave tid/64's 32 rows.
+  // (l%16) ^ swz_row(row)); keys past nk read as zeros.
   auto issue_tile = [&](int entry, auto bufc) {
     const int kb = entry >> 1;
     unsigned char* kt = bufp(bufc);
@@ -206,23 +209,37 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
       buf_load_lds<16>(kbuf, kt + j * 1024, voff, tile_base);
       buf_load_lds<16>(vbuf, kt + C::TILE_BYTES + j * 1024, voff, tile_base);
     }
-    const bool test = (entry & 1) || (kb == last_kb && ragged);
-    if (test) {
-      const int mkey = lane;  // key of the tile; the word is for this wave's rows
-      const int jk = kb * C::BN + mkey;
-      uint32_t word = 0xffffffffu;  // past the last key: masked for every row
-      if (jk < a.nk) {
-        auto bits = [&](int32_t s0, int32_t e0) -> uint32_t {
-          const int32_t lo = s0 <= q0w ? 0 : (s0 >= q0w + 32 ? 32 : s0 - q0w);
-          const int32_t hi = e0 <= q0w ? 0 : (e0 >= q0w + 32 ? 32 : e0 - q0w);
-          if (hi <= lo) return 0u;
-          const uint32_t upto_hi = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
-          return upto_hi & ~((1u << lo) - 1u);  // lo < 32 here
-        };
-        word = bits(mask.lts[jk], mask.lte[jk]) | bits(mask.uts[jk], mask.ute[jk]);
-      }
-      mwp(bufc)[w * C::BN + mkey] = word;
+  };
+  // Row mask of a partly masked tile: lane l loads the four vectors at key l of the tile before
+  // the tile's loads are issued and writes the word for this wave's 32 rows (bit t = row q0w + t
+  // masked) at the end of the iteration, so neither the tile loads nor the products wait for the
+  // vectors.
+  struct MaskKey {
+    int32_t s0, e0, s1, e1;
+    bool live;
+  };
+  auto is_test = [&](int entry) { return (entry & 1) || ((entry >> 1) == last_kb && ragged); };
+  auto mask_load = [&](int entry) {
+    MaskKey m{0, 0, 0, 0, false};
+    const int jk = (entry >> 1) * C::BN + lane;
+    m.live = jk < a.nk;  // keys past nk are masked for every row
+    if (m.live) {
+      m.s0 = mask.lts[jk];
+      m.e0 = mask.lte[jk];
+      m.s1 = mask.uts[jk];
+      m.e1 = mask.ute[jk];
     }
+    return m;
+  };
+  auto mask_store = [&](const MaskKey& m, auto bufc) {
+    auto bits = [&](int32_t s0, int32_t e0) -> uint32_t {
+      const int32_t lo = s0 <= q0w ? 0 : (s0 >= q0w + 32 ? 32 : s0 - q0w);
+      const int32_t hi = e0 <= q0w ? 0 : (e0 >= q0w + 32 ? 32 : e0 - q0w);
+      if (hi <= lo) return 0u;
+      const uint32_t upto_hi = hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u);
+      return upto_hi & ~((1u << lo) - 1u);  // lo < 32 here
+    };
+    mwp(bufc)[w * C::BN + lane] = m.live ? (bits(m.s0, m.e0) | bits(m.s1, m.e1)) : 0xffffffffu;
   };
 
   f32x16 dq_acc[C::NDB];
@@ -233,12 +250,18 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
 
   auto body = [&](const int it, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    const int kb = entry >> 1;
-    const bool test = (entry & 1) || (kb == last_kb && ragged);
-    const int next = it + 1 < cnt ? load_uniform(lst, it + 1) : 0;
+    const bool test = is_test(entry);
+    const bool has_next = it + 1 < cnt;
+    const int next = has_next ? load_uniform(lst, it + 1) : 0;
+    const bool next_test = has_next && is_test(next);
+    const auto other = std::integral_constant<int, buf ^ 1>{};
     wait_vmem();      // this wave's loads of tile `it` have landed in LDS
     __syncthreads();  // ... everyone's, and the mask words
-    if (it + 1 < cnt) issue_tile(next, std::integral_constant<int, buf ^ 1>{});
+    MaskKey mk{0, 0, 0, 0, false};
+    if (next_test) mk = mask_load(next);
+    // The last tile stages its own rows again into the free buffer, which is never read: the
+    // load count is then the same on every path and the compiler's waits stay exact.
+    issue_tile(has_next ? next : entry, other);
 
     const unsigned char* kt = bufp(bufc);
     const unsigned char* vt = kt + C::TILE_BYTES;
@@ -295,10 +318,15 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
       for (int db = 0; db < C::NDB; ++db)
         dq_acc[db] = E::mfma(tr_operand(kt, off_tk[db], t * KSTEP * C::ROW_BYTES), sf[t], dq_acc[db]);
 
+    if (next_test) mask_store(mk, other);
     entry = next;
   };
 
-  if (cnt > 0) issue_tile(entry, std::integral_constant<int, 0>{});
+  if (cnt > 0) {
+    const auto first = std::integral_constant<int, 0>{};
+    issue_tile(entry, first);
+    if (is_test(entry)) mask_store(mask_load(entry), first);
+  }
   // Unrolled by two so each buffer index is a compile-time constant; an odd last tile runs after
   // the loop, so the loop body has no conditional path the accumulators must merge across.
   int it = 0;
@@ -307,6 +335,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
     body(it + 1, std::integral_constant<int, 1>{});
   }
   if (it < cnt) body(it, std::integral_constant<int, 0>{});
+  wait_vmem();  // the last tile's extra loads land before the workgroup's LDS is released
 
   if (row_ok) {
     T* orow = dQp + (size_t)q_row * a.L.qs_r;

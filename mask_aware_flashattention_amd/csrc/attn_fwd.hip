@@ -57,12 +57,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   using frag = typename E::frag;
   constexpr int KPL = C::KPL, KSTEP = C::KSTEP;
 
-  // LDS: two buffers [K | V | mask words].  They are separate arrays so that the compiler can
-  // tell that loads into one buffer never overlap reads of the other, and adds no wait on the
-  // loads in flight before those reads.
-  constexpr int BUF_BYTES = 2 * C::TILE_BYTES + C::MW_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char lds0[BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char lds1[BUF_BYTES];
+  // LDS: two tile buffers [K | V] and two arrays of mask words.  They are separate arrays so
+  // that the compiler can tell that loads into one buffer never overlap reads of the other or
+  // the mask words, and adds no wait on the loads in flight before those accesses.
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[2 * C::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[2 * C::TILE_BYTES];
+  __shared__ uint32_t mw0[C::MW_BYTES / 4];
+  __shared__ uint32_t mw1[C::MW_BYTES / 4];
   auto bufp = [&](auto bc) -> unsigned char* {
     if constexpr (decltype(bc)::value == 0)
       return lds0;
@@ -70,7 +71,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       return lds1;
   };
   auto mwp = [&](auto bc) -> uint32_t* {
-    return reinterpret_cast<uint32_t*>(bufp(bc) + 2 * C::TILE_BYTES);
+    if constexpr (decltype(bc)::value == 0)
+      return mw0;
+    else
+      return mw1;
   };
 
   const int tid = threadIdx.x;
@@ -330,6 +334,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     body(it + 1, std::integral_constant<int, 1>{});
   }
   if (it < cnt) body(it, std::integral_constant<int, 0>{});
+  wait_vmem();  // the last tile's extra loads land before the workgroup's LDS is released
 
   const float l = pair_sum32(l_run);
   if (row_ok) {
