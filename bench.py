@@ -317,7 +317,7 @@ def main():
                 "tflops_call": round(flop_b / bwd_call_ms / 1e9, 2),
                 "frac_of_peak_call": round(flop_b / bwd_call_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
         # the backward's two kernels (dK/dV, then dQ) run back to back and are timed as one span
-        "roofline": {"kernel": "attn_bwd_kernel<bf16,128> + attn_dq_kernel<bf16,128>",
+        "roofline": {"kernel": "attn_dq_kernel<bf16,128> + attn_bwd_kernel<bf16,128>",
                      "bound": "mfma",
                      "achieved": round(bwd_achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(bwd_achieved / PEAK_BF16_TFLOPS, 4),
