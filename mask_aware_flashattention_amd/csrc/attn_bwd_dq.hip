@@ -246,13 +246,17 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) dq_acc[db] = f32x16{};
 
-  int entry = cnt > 0 ? load_uniform(lst, 0) : 0;
+  // List entries are read one tile ahead of their use (scalar loads: their latency then hides
+  // behind a tile instead of stalling the wave).  cnt > 0 here.
+  int entry = load_uniform(lst, 0);
+  int pre = load_uniform(lst, cnt > 1 ? 1 : 0);  // entry of the tile after `entry`
 
   auto body = [&](const int it, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const bool test = is_test(entry);
     const bool has_next = it + 1 < cnt;
-    const int next = has_next ? load_uniform(lst, it + 1) : 0;
+    const int next = has_next ? pre : 0;
+    pre = load_uniform(lst, it + 2 < cnt ? it + 2 : cnt - 1);
     const bool next_test = has_next && is_test(next);
     const auto other = std::integral_constant<int, buf ^ 1>{};
     wait_vmem();      // this wave's loads of tile `it` have landed in LDS
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
     entry = next;
   };
 
-  if (cnt > 0) {
+  {
     const auto first = std::integral_constant<int, 0>{};
     issue_tile(entry, first);
     if (is_test(entry)) mask_store(mask_load(entry), first);

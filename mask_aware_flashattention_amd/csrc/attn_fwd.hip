@@ -212,7 +212,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
   float m_run = -INFINITY;  // reference max (scale*log2(e) units) for this lane's row
   float l_run = 0.0f;       // this lane's share of the running sum (its 32 keys of each tile)
 
+  // List entries are read one tile ahead of their use (scalar loads: their latency then hides
+  // behind a tile instead of stalling the wave, and behind a barrier that waits for them anyway).
   int entry = load_uniform(lst, 0);
+  int pre = load_uniform(lst, cnt > 1 ? 1 : 0);  // entry of the tile after `entry`
 
   auto body = [&](const int it, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
@@ -221,7 +224,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     // The last tile stages its own rows again into the free buffer, which is never read: the
     // staging then needs no branch inside the products.
     const bool has_next = it + 1 < cnt;
-    const int next = has_next ? load_uniform(lst, it + 1) : entry;
+    const int next = has_next ? pre : entry;
+    pre = load_uniform(lst, it + 2 < cnt ? it + 2 : cnt - 1);
     const bool next_test = has_next && is_test(next);
     wait_vmem();      // this wave's loads of tile `it` have landed in LDS
     __syncthreads();  // ... everyone's, and the mask words; the other buffer is free
