@@ -120,3 +120,11 @@ def test_forward_is_deterministic(fm):
     o2, l2 = fm.fwd(q, k, vv, *v)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("tiles", [1, 2, 3, 4, 5, 6, 7])
+def test_every_walk_length(fm, tiles):
+    """Without a mask every key block lists every query tile, so nq = 64*tiles - 5 gives the
+    key-stationary walk exactly `tiles` tiles (the last one ragged): the tile pipeline's start
+    (one or two tiles), its three-buffer rotation and both remainders after it."""
+    run_case(fm, "bf16", 1, 1, 64 * tiles - 5, 160, "none", seed=tiles)
