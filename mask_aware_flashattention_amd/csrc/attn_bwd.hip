@@ -17,8 +17,9 @@
 //                the query blocks (BM = 64 rows) of its list in 32-row units; Q and dO rows
 //                are A operands read from LDS in a permuted row order so the accumulators
 //                double as operands, Q^T and dO^T come from the gfx950 LDS transpose read.
-//                Tiles are staged global -> registers -> LDS one tile ahead, double-buffered;
-//                one workgroup barrier per unit (P handed over) also publishes the next tile.
+//                Q/dO tiles go from HBM straight into three LDS buffers, requested two tiles
+//                ahead; one workgroup barrier per unit (P handed over) also publishes the next
+//                tile, and these barriers wait only for LDS traffic, not for loads in flight.
 //   dQ comes from the query-stationary kernel in attn_bwd_dq.hip, so no float32 atomics are
 //   needed and every gradient is deterministic.
 #include <math.h>
