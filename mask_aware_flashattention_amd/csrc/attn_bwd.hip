@@ -48,7 +48,9 @@ struct BwdTile {
   // wave w (16 rows in its first 16 floats; LSE2 in slots 0-3, D in 4-7)
   static constexpr int ROWS_BYTES = 8 * 64 * (int)sizeof(float);
   static constexpr int BUF_BYTES = 2 * TILE_BYTES + ROWS_BYTES;
-  static constexpr int XCH_BYTES = 4 * 16 * 64 * (int)sizeof(float);  // one unit's P, 4 groups
+  static constexpr int US_ = 32 / KSTEP;
+  // one unit's P as operand fragments, 4 groups
+  static constexpr int XCH_BYTES = 4 * US_ * 64 * KPL * (int)sizeof(T);
   static_assert(CPR == 16, "tile loads assume 256-byte rows");
   static_assert(TILE_BYTES == 16 * 1024, "16 blocks of 1 KiB per tile");
 };
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds0[C::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char lds1[C::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char lds2[C::BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) float xch[2 * C::XCH_BYTES / sizeof(float)];  // [2 units][4 groups][4][64][4]
+  __shared__ __attribute__((aligned(16))) unsigned char xch[2 * C::XCH_BYTES];  // P of two units
   auto bufp = [&](auto bc) -> unsigned char* {
     constexpr int bi = decltype(bc)::value;
     if constexpr (bi == 0)
@@ -288,9 +290,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   };
 
   // ---- one 32-query unit ----------------------------------------------------------------------
-  // P of unit parity h in LDS: [group][r/4][lane][r%4], so that each 16-byte access of a lane
-  // group is contiguous.
-  auto xoff = [&](int h, int r4) { return ((h * 4 + kg) * 4 + r4) * 64 * 4 + lane * 4; };
+  // P of unit parity h in LDS as the P wave's operand fragments (bf16 in the bf16 kernel, so
+  // the hand-over moves half the bytes of float32): [h][group][k-step u][lane], each lane's
+  // fragment contiguous.
   // Row operands (Q for the P wave, dO for the dS wave) of unit h of the tile at qt.
   auto read_ops = [&](const unsigned char* qt, int h, frag* op) {
 #pragma unroll
@@ -330,6 +332,24 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
         for (int e = 0; e < KPL; ++e) fr[u][e] = E::from_float(pv[u * KPL + e]);
       }
     }
+  };
+  auto xfrag = [&](int h, int u) -> frag* {
+    return reinterpret_cast<frag*>(xch) + ((h * 4 + kg) * US + u) * 64 + lane;
+  };
+  // dS = P (dP - D) of a unit, from its P fragments in exchange slot h; dp holds dP - D.
+  auto ds_frags = [&](int h, const f32x16& dp, frag* fr) {
+    float pv[16];
+#pragma unroll
+    for (int u = 0; u < US; ++u) {
+      const frag f = *xfrag(h, u);
+      if constexpr (KPL == 1) {
+        pv[u] = f * dp[u];
+      } else {
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) pv[u * KPL + e] = (float)f[e] * dp[u * KPL + e];
+      }
+    }
+    to_frags(pv, fr);
   };
   // dV^T += dO^T P or dK^T += Q^T dS over the 32 queries of unit h of the tile at qt.
   auto accumulate = [&](const unsigned char* qt, int h, const frag* fr) {
@@ -371,30 +391,19 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) pv[r] = select_bit(mw, perm_index<KPL>(r, 0), pv[r], 0u);
       }
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<float4*>(xch + xoff(h, r4)) =
-            make_float4(pv[4 * r4], pv[4 * r4 + 1], pv[4 * r4 + 2], pv[4 * r4 + 3]);
-      publish();  // workgroup barrier: P of this unit (and possibly the next tile) visible
       frag fr[US];
       to_frags(pv, fr);
+#pragma unroll
+      for (int u = 0; u < US; ++u) *xfrag(h, u) = fr[u];
+      publish();  // workgroup barrier: P of this unit (and possibly the next tile) visible
       if (next) read_ops(qn, hn, op);
       accumulate(qt, h, fr);
     } else {
       if (pending) {
         // dS = P (dP - D) of the pending unit (the other half: slot 1 - h); dp_prev already
         // holds dP - D
-        float pv[16];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const float4 p = *reinterpret_cast<const float4*>(xch + xoff(1 - h, r4));
-          pv[4 * r4 + 0] = p.x * dp_prev[4 * r4 + 0];
-          pv[4 * r4 + 1] = p.y * dp_prev[4 * r4 + 1];
-          pv[4 * r4 + 2] = p.z * dp_prev[4 * r4 + 2];
-          pv[4 * r4 + 3] = p.w * dp_prev[4 * r4 + 3];
-        }
         frag fr[US];
-        to_frags(pv, fr);
+        ds_frags(1 - h, dp_prev, fr);
         accumulate(qp, 1 - h, fr);
       }
       // dP - D = dO V^T - D of this unit: the products accumulate onto the rows' -D values
@@ -494,17 +503,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   if (dsw) {
     const int lb = (total - 1) % 3;
     const unsigned char* ql = lb == 0 ? lds0 : (lb == 1 ? lds1 : lds2);
-    float pv[16];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const float4 p = *reinterpret_cast<const float4*>(xch + xoff(1, r4));
-      pv[4 * r4 + 0] = p.x * dp_prev[4 * r4 + 0];
-      pv[4 * r4 + 1] = p.y * dp_prev[4 * r4 + 1];
-      pv[4 * r4 + 2] = p.z * dp_prev[4 * r4 + 2];
-      pv[4 * r4 + 3] = p.w * dp_prev[4 * r4 + 3];
-    }
     frag fr[US];
-    to_frags(pv, fr);
+    ds_frags(1, dp_prev, fr);
     accumulate(ql, 1, fr);
   }
 

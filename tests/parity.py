@@ -9,6 +9,8 @@ for a set of key columns only the rows with an unmasked entry in those columns c
 
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -73,6 +75,8 @@ def assert_close(name, got, want, tol):
     assert got.shape == want.shape, (name, got.shape, want.shape)
     assert not np.isnan(got).any(), f"{name}: NaN in GPU output"
     err = np.abs(got - want).max() if got.size else 0.0
+    if os.environ.get("FM_PARITY_REPORT"):
+        print(f"parity {name}: max-abs error {err:.3e} (tolerance {tol:.1e})", flush=True)
     assert err <= tol, f"{name}: max-abs error {err:.3e} > {tol:.1e}"
     return err
 
