@@ -48,9 +48,8 @@ struct BwdTile {
   // wave w (16 rows in its first 16 floats; LSE2 in slots 0-3, D in 4-7)
   static constexpr int ROWS_BYTES = 8 * 64 * (int)sizeof(float);
   static constexpr int BUF_BYTES = 2 * TILE_BYTES + ROWS_BYTES;
-  static constexpr int US_ = 32 / KSTEP;
-  // one unit's P as operand fragments, 4 groups
-  static constexpr int XCH_BYTES = 4 * US_ * 64 * KPL * (int)sizeof(T);
+  // one unit's P as operand fragments (US per lane), 4 groups
+  static constexpr int XCH_BYTES = 4 * US * 64 * KPL * (int)sizeof(T);
   static_assert(CPR == 16, "tile loads assume 256-byte rows");
   static_assert(TILE_BYTES == 16 * 1024, "16 blocks of 1 KiB per tile");
 };
