@@ -251,11 +251,24 @@ int32_t flashmask_fwd(const fm_shape* s, const void* Q, const void* K, const voi
   return flashmask_fwd_ex(&l, Q, K, V, LTS, LTE, UTS, UTE, scale, O, LSE, ws, ws_bytes, stream);
 }
 
+// Geometry of the dK/dV kernel's column lists: key blocks of t.bn_bwd keys, or of twice that
+// where the finer grid exceeds the list limits (very long sequences); *bn gets the width.
+int32_t bwd_col_geometry(const fm_layout* l, const fm::TileShape& t, Geometry* g, int32_t* bn) {
+  *bn = t.bn_bwd;
+  int32_t st = check_layout(l, t.bm_bwd, t.bn_bwd, true, g);
+  if (st == FM_ERR_SHAPE && check_layout(l, t.bm_bwd, 2 * t.bn_bwd, true, g) == FM_OK) {
+    *bn = 2 * t.bn_bwd;
+    st = FM_OK;
+  }
+  return st;
+}
+
 size_t flashmask_bwd_ex_workspace_bytes(const fm_layout* l) {
   if (!l || check_dtype(l->dtype, l->d) != FM_OK) return 0;
   const fm::TileShape t = tiles(l->dtype);
   Geometry g, gf;
-  if (check_layout(l, t.bm_bwd, t.bn_bwd, true, &g) != FM_OK) return 0;
+  int32_t bn_b;
+  if (bwd_col_geometry(l, t, &g, &bn_b) != FM_OK) return 0;
   if (check_layout(l, t.bm_fwd, t.bn_fwd, true, &gf) != FM_OK) return 0;
   return bwd_layout(l, g, gf).total;
 }
@@ -269,7 +282,8 @@ int32_t flashmask_bwd_ex(const fm_layout* l, const void* Q, const void* K, const
   if (st != FM_OK) return st;
   const fm::TileShape t = tiles(l->dtype);
   Geometry g, gf;
-  if ((st = check_layout(l, t.bm_bwd, t.bn_bwd, true, &g)) != FM_OK) return st;
+  int32_t bn_b;
+  if ((st = bwd_col_geometry(l, t, &g, &bn_b)) != FM_OK) return st;
   if ((st = check_layout(l, t.bm_fwd, t.bn_fwd, true, &gf)) != FM_OK) return st;
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FM_ERR_NULL;
   if ((st = check_vectors(LTS, LTE, UTS, UTE)) != FM_OK) return st;
@@ -298,7 +312,7 @@ int32_t flashmask_bwd_ex(const fm_layout* l, const void* Q, const void* K, const
   const fm::MaskVecs mv{LTS, LTE, UTS, UTE};
   const fm::Layout lay = to_internal(l);
 
-  hipError_t e = fm::launch_block_minmax(mv, l->nk, t.bn_bwd, mm, hs, sets, l->nk);
+  hipError_t e = fm::launch_block_minmax(mv, l->nk, bn_b, mm, hs, sets, l->nk);
   if (e == hipSuccess)
     e = fm::launch_classify(mm, (int32_t)g.n_kb, l->nq, t.bm_bwd, nullptr, nullptr, nullptr, kcnt,
                             klist, hs, sets);
@@ -315,7 +329,7 @@ int32_t flashmask_bwd_ex(const fm_layout* l, const void* Q, const void* K, const
   }
   if (e == hipSuccess) {
     fm::BwdArgs a{Q,     K,    V,      dO,   mv,   dK, dV, delta, lse2, kcnt, klist,
-                  korder, (int32_t)g.n_qb, lay, l->nq, l->nk, scale};
+                  korder, (int32_t)g.n_qb, bn_b, lay, l->nq, l->nk, scale};
     e = fm::launch_attn_bwd(l->dtype, a, hs, g_bwd_end);
   }
   return hip_status(e);

@@ -6,8 +6,8 @@
 // partly masked tiles, as the forward; "FlashMask-3 sends each GPU its mask ...",
 // tile-classification paragraph).
 //
-//   K5 dK / dV:  one workgroup of 8 waves per key block of BN = 128 keys: 4 key groups of 32
-//                keys, and per key group a pair of waves on one SIMD that split the work:
+//   K5 dK / dV:  one workgroup of 4 waves per block of BN = 64 keys (two workgroups per CU):
+//                2 key groups of 32 keys, and per key group a pair of waves that split the work:
 //                  the P wave keeps K rows in registers, computes S = Q K^T, P = exp2(S*scale*
 //                  log2e - LSE*log2e) (0 where masked) and accumulates dV^T += dO^T P;
 //                  the dS wave keeps V rows, computes dP = dO V^T, takes P from the P wave
@@ -17,9 +17,9 @@
 //                the query blocks (BM = 64 rows) of its list in 32-row units; Q and dO rows
 //                are A operands read from LDS in a permuted row order so the accumulators
 //                double as operands, Q^T and dO^T come from the gfx950 LDS transpose read.
-//                Q/dO tiles go from HBM straight into three LDS buffers, requested two tiles
-//                ahead; one workgroup barrier per unit (P handed over) also publishes the next
-//                tile, and these barriers wait only for LDS traffic, not for loads in flight.
+//                Q/dO tiles go from HBM straight into two LDS buffers, requested a unit ahead;
+//                one workgroup barrier per unit (P handed over) also publishes the next tile,
+//                and these barriers wait only for LDS traffic, not for loads in flight.
 //   dQ comes from the query-stationary kernel in attn_bwd_dq.hip, so no float32 atomics are
 //   needed and every gradient is deterministic.
 #include <math.h>
@@ -35,7 +35,12 @@ namespace {
 
 template <typename T, int D>
 struct BwdTile {
-  static constexpr int BN = 128, BM = 64, NT = 512;  // 8 waves: 4 key groups x 2 roles
+  // NG key groups of 32 keys, a P wave and a dS wave each: 4 waves, and two workgroups per CU,
+  // which run independently of each other (better latency hiding than one 8-wave workgroup whose
+  // waves all meet at every barrier).
+  static constexpr int NG = 2;
+  static constexpr int BN = 32 * NG, BM = 64, NT = 128 * NG;
+  static constexpr int BPW = 16 / NG, SPW = 4 / NG;  // per wave and tile: 1-KiB blocks, row slots
   static constexpr int KPL = Elem<T>::KPL, KSTEP = 2 * KPL;
   static constexpr int CH = 16 / (int)sizeof(T);
   static constexpr int CPR = D / CH;  // 16-byte chunks per Q / dO / K row
@@ -44,12 +49,12 @@ struct BwdTile {
   static constexpr int QK_STEPS = D / KSTEP;
   static constexpr int US = 32 / KSTEP;  // k-steps over a unit's 32 queries
   static constexpr int TILE_BYTES = BM * ROW_BYTES;
-  // Q | dO | rows: LSE2 and D of the tile's rows in 8 slots of 64 floats, slot w filled by
-  // wave w (16 rows in its first 16 floats; LSE2 in slots 0-3, D in 4-7)
+  // Q | dO | rows: LSE2 and D of the tile's rows in 8 slots of 64 floats, wave w filling slots
+  // SPW*w .. SPW*w + SPW - 1 (16 rows in a slot's first 16 floats; LSE2 in slots 0-3, D in 4-7)
   static constexpr int ROWS_BYTES = 8 * 64 * (int)sizeof(float);
   static constexpr int BUF_BYTES = 2 * TILE_BYTES + ROWS_BYTES;
   // one unit's P as operand fragments (US per lane), 4 groups
-  static constexpr int XCH_BYTES = 4 * US * 64 * KPL * (int)sizeof(T);
+  static constexpr int XCH_BYTES = NG * US * 64 * KPL * (int)sizeof(T);
   static_assert(CPR == 16, "tile loads assume 256-byte rows");
   static_assert(TILE_BYTES == 16 * 1024, "16 blocks of 1 KiB per tile");
 };
@@ -61,51 +66,53 @@ struct MaskRegs {
 // GQ: more than one query head per key/value head (a.L.G > 1); the G = 1 instantiation walks a
 // single list and needs no guard for rows past nq.
 template <typename T, int D, bool GQ>
-__global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_kernel(BwdArgs a) {
   using C = BwdTile<T, D>;
   using E = Elem<T>;
   using frag = typename E::frag;
   constexpr int KPL = C::KPL, KSTEP = C::KSTEP, US = C::US;
 
-  // Three tile buffers, Q|dO|LSE2|D each, as separate arrays: the compiler then sees that the
-  // loads straight into one buffer never alias reads of another and adds no waits for them.
+  // Two tile buffers, Q|dO|LSE2|D each, as separate arrays: the compiler then sees that the
+  // loads straight into one buffer never alias reads of the other and adds no waits for them.
+  // (Two workgroups of 76 KiB fit in a CU's LDS; three buffers would not.)
   __shared__ __attribute__((aligned(16))) unsigned char lds0[C::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char lds1[C::BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char lds2[C::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char xch[2 * C::XCH_BYTES];  // P of two units
   auto bufp = [&](auto bc) -> unsigned char* {
     constexpr int bi = decltype(bc)::value;
     if constexpr (bi == 0)
       return lds0;
-    else if constexpr (bi == 1)
-      return lds1;
     else
-      return lds2;
+      return lds1;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-  const int kg = wv & 3;                                     // key group
-  const bool dsw = wv >= 4;                                  // the dS wave of the pair
+  const int kg = wv % C::NG;                                 // key group
+  const bool dsw = wv >= C::NG;                              // the dS wave of the pair
 
-  // The workgroup owns key block kb of key/value head hk of batch b; with G query heads per
-  // key/value head it walks the tile lists of all G heads in turn, accumulating into the same
-  // dK and dV registers (no atomics).
-  const int n_kb = (a.nk + C::BN - 1) / C::BN;
+  // The workgroup owns BN keys of list key block kb of key/value head hk of batch b: the whole
+  // block, or for very long sequences (lists over 128-key blocks) one half of it, the two halves
+  // being neighbouring work items that walk the same list.  With G query heads per key/value
+  // head it walks the tile lists of all G heads in turn, accumulating into the same dK and dV
+  // registers (no atomics).
+  const int lbn = a.list_bn;
+  const int hshift = lbn > C::BN ? 1 : 0;  // log2 of the halves per list block
+  const int n_kb = (a.nk + lbn - 1) / lbn;
   const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
   // (every index here is the same for the whole workgroup; readfirstlane keeps it in scalar
   // registers, and with it every pointer and buffer descriptor derived from it)
   const int G = GQ ? a.L.G : 1;
   const int Hk = a.L.H / G;
-  const int bhk = __builtin_amdgcn_readfirstlane(work / n_kb);
+  const int bhk = __builtin_amdgcn_readfirstlane(work / (n_kb << hshift));
   const int b = __builtin_amdgcn_readfirstlane(bhk / Hk);
   const int hk = bhk - b * Hk, h0 = hk * G;
-  const int kb = __builtin_amdgcn_readfirstlane(a.order[(size_t)mask_set(a.L, b, h0) * n_kb + work % n_kb]);
-  const int key = kb * C::BN + kg * 32 + l32;  // this lane's key (a column of S)
+  const int rem = work - bhk * (n_kb << hshift), half = rem & hshift;
+  const int kb = __builtin_amdgcn_readfirstlane(a.order[(size_t)mask_set(a.L, b, h0) * n_kb + (rem >> hshift)]);
+  const int key = kb * lbn + half * C::BN + kg * 32 + l32;  // this lane's key (a column of S)
   const bool key_ok = key < a.nk;
   const int64_t kbase = b * a.L.ks_b + hk * a.L.ks_h;
   int total = 0;
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
     // No listed tile: every query row is masked for these keys, so dK = dV = 0.  Each lane
     // clears half of its key's row (128 bytes) in the tensor of its wave's role.
     if (key_ok) {
-      T* row = static_cast<T*>(wv >= 4 ? a.dk : a.dv) + kbase + (size_t)key * a.L.ks_r;
+      T* row = static_cast<T*>(dsw ? a.dk : a.dv) + kbase + (size_t)key * a.L.ks_r;
       uint4* p = reinterpret_cast<uint4*>(row + g * (D / 2));
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
     else
       bop[s] = __builtin_bit_cast(frag, buf_load4(kvbuf, off, 0));
   }
-  const bool ragged_block = (kb == n_kb - 1) && (a.nk % C::BN) != 0;
+  const bool ragged_block = (kb == n_kb - 1) && (a.nk % lbn) != 0;
 
   // ---- per-lane LDS byte offsets, constant for the whole kernel ------------------------------
   // Transpose-read lane geometry: lane i of 16-lane block b addresses row k0 + 8*(b/2) + i/4,
@@ -237,13 +244,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   // would place there for a register loaded now would also wait for those.
   wait_vmem();
 
-  // A tile's 64 rows of Q, then of dO, are 32 blocks of 1 KiB; wave w moves blocks 4w..4w+3
-  // (waves 0-3 Q, 4-7 dO), lane l the 16-byte slot l of a block: row 4j + l/16 of its tensor,
-  // physical chunk l%16, which holds logical chunk (l%16) ^ swz_row(row).  Rows past nq read as
-  // zeros.  Each wave also moves 16 of the tile's LSE2 (waves 0-3) or D (waves 4-7) values, in
-  // lanes 0-15 of its row slot (lanes 16-63 read out of range and write zeros into the rest of the
-  // slot).  The loads go straight into LDS (no registers, no LDS writes by the waves): five per
-  // wave and tile, the same for every wave, so one vmcnt value covers a tile.
+  // A tile's 64 rows of Q, then of dO, are 32 blocks of 1 KiB; wave w moves blocks
+  // BPW*w .. BPW*w + BPW - 1 (the P waves Q, the dS waves dO), lane l the 16-byte slot l of a
+  // block: row 4j + l/16 of its tensor, physical chunk l%16, which holds logical chunk
+  // (l%16) ^ swz_row(row).  Rows past nq read as zeros.  Each wave also fills SPW row slots, 16
+  // LSE2 (slots 0-3) or D (slots 4-7) values each, in lanes 0-15 (lanes 16-63 read out of range
+  // and write zeros into the rest of the slot).  The loads go straight into LDS (no registers, no
+  // LDS writes by the waves).
   // The buffers span all G heads, so rows past nq of one head are another head's rows: their
   // offsets are moved to the buffer's end, where loads return zeros (dO = 0 and D = 0 make such a
   // row contribute nothing).
@@ -251,21 +258,23 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
     unsigned char* t = bufp(bc);
     const int q0 = (entry >> 1) * C::BM;
     const uint32_t tile_base = (uint32_t)gi * qhs + (uint32_t)q0 * qrs;
-    const buf_rsrc src = wv < 4 ? qbuf : dobuf;
+    const buf_rsrc src = wv < C::NG ? qbuf : dobuf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * ((4 * wv + i) & 15) + (lane >> 4);
+    for (int i = 0; i < C::BPW; ++i) {
+      const int row = 4 * ((C::BPW * wv + i) & 15) + (lane >> 4);
       const uint32_t voff = !GQ || q0 + row < a.nq
                                 ? (uint32_t)row * qrs + (uint32_t)(((lane & 15) ^ swz_row<T>(row)) * 16)
                                 : q_span - tile_base;
-      buf_load_lds<16>(src, t + (4 * wv + i) * 1024, voff, tile_base);
+      buf_load_lds<16>(src, t + (C::BPW * wv + i) * 1024, voff, tile_base);
     }
-    {
-      const int r = 16 * (wv & 3) + lane;  // tile row of this lane (lanes below 16)
+#pragma unroll
+    for (int i = 0; i < C::SPW; ++i) {
+      const int slot = C::SPW * wv + i;
+      const int r = 16 * (slot & 3) + lane;  // tile row of this lane (lanes below 16)
       const uint32_t roff = ((uint32_t)gi * a.nq + (uint32_t)q0) * sizeof(float);
       const uint32_t r_span = (uint32_t)G * a.nq * sizeof(float);
       const uint32_t loff = lane < 16 && (!GQ || q0 + r < a.nq) ? (uint32_t)r * sizeof(float) : r_span - roff;
-      buf_load_lds<4>(wv < 4 ? lbuf : dlbuf, t + 2 * C::TILE_BYTES + wv * 64 * sizeof(float), loff, roff);
+      buf_load_lds<4>(slot < 4 ? lbuf : dlbuf, t + 2 * C::TILE_BYTES + slot * 64 * sizeof(float), loff, roff);
     }
   };
   // Every tile step issues exactly one tile's five loads (near the end of the walk a real tile is
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
     }
   };
   auto xfrag = [&](int h, int u) -> frag* {
-    return reinterpret_cast<frag*>(xch) + ((h * 4 + kg) * US + u) * 64 + lane;
+    return reinterpret_cast<frag*>(xch) + ((h * C::NG + kg) * US + u) * 64 + lane;
   };
   // dS = P (dP - D) of a unit, from its P fragments in exchange slot h; dp holds dP - D.
   auto ds_frags = [&](int h, const f32x16& dp, frag* fr) {
@@ -421,39 +430,30 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   };
 
   // ---- the walk over the key block's query tiles ---------------------------------------------
-  // Tile t sits in buffer t % 3.  Right after the barrier of tile t's first unit, the loads of
-  // tile t+2 into the buffer tile t-1 used are issued (after that barrier no wave reads tile t-1:
-  // the dS wave finished its lagging unit of tile t-1 before it; the last two tiles load a tile
-  // again instead); before the barrier of tile t's second unit each wave waits for its loads of
-  // tile t+1 (issued a tile earlier), and the barrier publishes that tile.  A load so has three
-  // units to land.
+  // Tile t sits in buffer t % 2.  Right after the barrier of tile t's first unit, the loads of
+  // tile t+1 into the buffer tile t-1 used are issued (after that barrier no wave reads tile t-1:
+  // the dS wave finished its lagging unit of tile t-1 before it); before the barrier of tile t's
+  // second unit each wave waits for its loads, and that barrier publishes tile t+1.  A load so
+  // has one unit to land; the other workgroup on the CU covers the waits.
   // The walk is written out once per role (same barriers in the same order), so that neither
   // role's loop carries the other's registers.
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
   {
     load_tile(first.gi, entry_of(first), I0{});
-    Cursor second = first;
-    if (total > 1) advance(second);
-    load_tile(second.gi, entry_of(second), I1{});  // tile 1, or tile 0 again (never read)
-    wait_vmem_n<5>();                              // tile 0 has landed
+    wait_vmem();
     lds_barrier();
   }
   f32x16 dp_prev = {};  // dS wave: dP of the pending unit
   auto walk = [&](auto role) {
-    Cursor cur = first;        // the tile being walked
-    Cursor ahead = first;      // the tile two ahead, loaded during this one
-    advance(ahead);
-    if (total > 1) advance(ahead);
+    Cursor cur = first;  // the tile being walked
     int entry = entry_of(cur);
     frag op[C::QK_STEPS];
     read_ops(bufp(I0{}), 0, op);
-    // tile t in buffer bc = t % 3 (a compile-time constant, so LDS offsets fold into the
-    // instructions); tile t+1 is in buffer (bc+1) % 3, tile t-1 was in (bc+2) % 3
+    // tile t in buffer bc = t % 2; tile t+1 goes into the other buffer, which tile t-1 used
     auto tile = [&](const int t, auto bc) {
       constexpr int bi = decltype(bc)::value;
-      using BNext = std::integral_constant<int, (bi + 1) % 3>;
-      using BPrev = std::integral_constant<int, (bi + 2) % 3>;
+      using BOther = std::integral_constant<int, bi ^ 1>;
       const bool test = (entry & 1) || ragged_block;
       uint64_t mrow = 0ull;  // the row test belongs to the P wave only
       if constexpr (!decltype(role)::value) {
@@ -464,32 +464,27 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
       }
       const unsigned char* qt = bufp(bc);
       const bool more = t + 1 < total;
-      const bool more2 = t + 2 < total;
+      Cursor nxt = cur;
+      if (more) advance(nxt);
       step(role, qt, H0{}, test, mrow, [&] {
         lds_barrier();
-        // tile t+2 (or tile t again, never read) into tile t-1's buffer: no wave reads that
-        // buffer after this barrier
-        const Cursor& src = more2 ? ahead : cur;
-        load_tile(src.gi, entry_of(src), BPrev{});
-        if (more2) advance(ahead);
-      }, op, dp_prev, true, qt, 1, bufp(BPrev{}), t > 0);
+        if (more) load_tile(nxt.gi, entry_of(nxt), BOther{});  // no wave reads tile t-1 now
+      }, op, dp_prev, true, qt, 1, bufp(BOther{}), t > 0);
       step(role, qt, H1{}, test, mrow, [&] {
-        wait_vmem_n<5>();  // this wave's part of tile t+1 has landed ...
-        lds_barrier();     // ... and everyone's
-      }, op, dp_prev, more, bufp(BNext{}), 0, qt, true);
+        wait_vmem();    // this wave's part of tile t+1 has landed ...
+        lds_barrier();  // ... and everyone's
+      }, op, dp_prev, more, bufp(BOther{}), 0, qt, true);
       if (more) {
-        advance(cur);
+        cur = nxt;
         entry = entry_of(cur);
       }
     };
     int t = 0;
-    for (; t + 2 < total; t += 3) {
+    for (; t + 1 < total; t += 2) {
       tile(t, I0{});
       tile(t + 1, I1{});
-      tile(t + 2, I2{});
     }
     if (t < total) tile(t, I0{});
-    if (t + 1 < total) tile(t + 1, I1{});
   };
   if (dsw)
     walk(std::true_type{});
@@ -500,8 +495,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(BwdArgs a) {
   wait_vmem();
   // the dS wave's last pending unit: the second half of the last tile
   if (dsw) {
-    const int lb = (total - 1) % 3;
-    const unsigned char* ql = lb == 0 ? lds0 : (lb == 1 ? lds1 : lds2);
+    const unsigned char* ql = ((total - 1) & 1) ? lds1 : lds0;
     frag fr[US];
     ds_frags(1, dp_prev, fr);
     accumulate(ql, 1, fr);
@@ -533,8 +527,9 @@ template <typename T, int D>
 hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_end) {
   using C = BwdTile<T, D>;
   auto kernel = a.L.G > 1 ? &attn_bwd_kernel<T, D, true> : &attn_bwd_kernel<T, D, false>;
-  const int64_t n_kb = (a.nk + C::BN - 1) / C::BN;
-  const int64_t grid = n_kb * a.L.B * (a.L.H / a.L.G);
+  if (a.list_bn != C::BN && a.list_bn != 2 * C::BN) return hipErrorInvalidValue;
+  const int64_t n_kb = (a.nk + a.list_bn - 1) / a.list_bn;
+  const int64_t grid = (a.list_bn / C::BN) * n_kb * a.L.B * (a.L.H / a.L.G);
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (ev_end) (void)hipEventRecord(ev_end, stream);

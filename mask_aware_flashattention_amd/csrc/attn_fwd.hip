@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
 
 TileShape tile_shape(int dtype) {
   (void)dtype;
-  return TileShape{FwdTile<bf16, 128>::BM, FwdTile<bf16, 128>::BN, 64, 128};
+  return TileShape{FwdTile<bf16, 128>::BM, FwdTile<bf16, 128>::BN, 64, 64};
 }
 
 hipError_t launch_attn_fwd(int dtype, const FwdArgs& a, hipStream_t stream, hipEvent_t ev_begin,

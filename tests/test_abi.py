@@ -56,7 +56,7 @@ def test_tile_sizes(lib):
     v = [ctypes.c_int32() for _ in range(4)]
     refs = [ctypes.byref(x) for x in v]
     assert lib.flashmask_tile_sizes(0, 128, *refs) == FM_OK
-    assert [x.value for x in v] == [128, 64, 64, 128]
+    assert [x.value for x in v] == [128, 64, 64, 64]
     assert lib.flashmask_tile_sizes(1, 64, *refs) == FM_OK
     assert lib.flashmask_tile_sizes(0, 64, *refs) == FM_ERR_UNSUPPORTED
     assert lib.flashmask_tile_sizes(1, 128, *refs) == FM_ERR_UNSUPPORTED
@@ -74,13 +74,22 @@ def test_workspace_sizes(lib):
     r = lambda x: -(-x // 256) * 256
     assert lib.flashmask_fwd_workspace_bytes(ctypes.byref(s)) == (
         r(32 * n_kb) + r(4 * n_qb) + r(4 * n_qb * n_kb) + r(4 * n_qb))
-    n_qb, n_kb = 5, 2      # dK/dV lists at tiles 64 x 128
+    n_qb, n_kb = 5, 4      # dK/dV lists at tiles 64 x 64
     f_qb, f_kb = 3, 4      # dQ lists at the forward tiles 128 x 64
     rows = 1 * 2 * 300
     want = (r(32 * n_kb) + r(4 * n_kb) + r(4 * n_qb * n_kb)
             + r(32 * f_kb) + r(4 * f_qb) + r(4 * f_qb * f_kb)
             + r(4 * n_kb) + r(4 * f_qb) + 2 * r(4 * rows))
     assert lib.flashmask_bwd_workspace_bytes(ctypes.byref(s)) == want
+    # the longest square problem: the 64 x 64 grid would hold 2^32 tiles, so the dK/dV lists
+    # fall back to 128-key blocks (64 x 128 grid)
+    n = 2 ** 22 - 128
+    n_qb, n_kb = n // 64, n // 128
+    f_qb, f_kb = n // 128, n // 64
+    want = (r(32 * n_kb) + r(4 * n_kb) + r(4 * n_qb * n_kb)
+            + r(32 * f_kb) + r(4 * f_qb) + r(4 * f_qb * f_kb)
+            + r(4 * n_kb) + r(4 * f_qb) + 2 * r(4 * n))
+    assert lib.flashmask_bwd_workspace_bytes(ctypes.byref(shape(H=1, nq=n, nk=n))) == want
     assert lib.flashmask_fwd_workspace_bytes(ctypes.byref(shape(d=64))) == 0
     assert lib.flashmask_classify_workspace_bytes(1000, 64) == 512
     assert lib.flashmask_classify_workspace_bytes(0, 64) == 0
@@ -221,7 +230,7 @@ def test_ex_workspace_matches_plain_and_scales_with_mask_sets(lib):
     l = layout(B=2, mask_b=2, mask_h=2)
     assert lib.flashmask_fwd_ex_workspace_bytes(ctypes.byref(l)) == (
         r(32 * n_kb * sets) + r(4 * n_qb * sets) + r(4 * n_qb * n_kb * sets) + r(4 * n_qb * sets))
-    n_qb, n_kb = 5, 2
+    n_qb, n_kb = 5, 4
     f_qb, f_kb = 3, 4
     rows = 2 * 2 * 300
     want = (r(32 * n_kb * sets) + r(4 * n_kb * sets) + r(4 * n_qb * n_kb * sets)

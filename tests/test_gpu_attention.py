@@ -125,6 +125,7 @@ def test_forward_is_deterministic(fm):
 @pytest.mark.parametrize("tiles", [1, 2, 3, 4, 5, 6, 7])
 def test_every_walk_length(fm, tiles):
     """Without a mask every key block lists every query tile, so nq = 64*tiles - 5 gives the
-    key-stationary walk exactly `tiles` tiles (the last one ragged): the tile pipeline's start
-    (one or two tiles), its three-buffer rotation and both remainders after it."""
+    key-stationary walk exactly `tiles` tiles (the last one ragged): the tile pipeline's start,
+    its two-buffer rotation over an even or odd number of tiles, and both halves of a key block
+    (nk = 160: one full 128-key block and a ragged one)."""
     run_case(fm, "bf16", 1, 1, 64 * tiles - 5, 160, "none", seed=tiles)
