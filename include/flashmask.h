@@ -63,9 +63,10 @@ const char* flashmask_strerror(int32_t status);
 /*
  * Tile shape used by the attention kernels for (dtype, d): the forward runs BM_fwd query rows
  * against BN_fwd key columns per tile, the backward BM_bwd x BN_bwd.  These are the tile shapes
- * at which tiles are classified (see flashmask_classify); where the backward's BM_bwd x BN_bwd
- * grid would hold 2^31 tiles or more (nq, nk beyond about 2.9 million), its key blocks are
- * 2 * BN_bwd wide instead.  Returns FM_ERR_DTYPE / FM_ERR_UNSUPPORTED / FM_ERR_NULL, or FM_OK.
+ * at which tiles are classified (see flashmask_classify); for nq >= 65536, or where the
+ * backward's BM_bwd x BN_bwd grid would hold 2^31 tiles or more, its key blocks are 2 * BN_bwd
+ * wide instead (another shape of the dK/dV kernel).  Returns FM_ERR_DTYPE / FM_ERR_UNSUPPORTED /
+ * FM_ERR_NULL, or FM_OK.
  */
 int32_t flashmask_tile_sizes(int32_t dtype, int32_t d, int32_t* BM_fwd, int32_t* BN_fwd,
                              int32_t* BM_bwd, int32_t* BN_bwd);

@@ -252,15 +252,17 @@ int32_t flashmask_fwd(const fm_shape* s, const void* Q, const void* K, const voi
 }
 
 // Geometry of the dK/dV kernel's column lists: key blocks of t.bn_bwd keys, or of twice that
-// where the finer grid exceeds the list limits (very long sequences); *bn gets the width.
+// for long query sequences (the kernel shape that keeps Q/dO loads further ahead) and where the
+// finer grid would exceed the list limits; *bn gets the width, which selects the kernel shape.
+constexpr int32_t kLongQuery = 65536;
 int32_t bwd_col_geometry(const fm_layout* l, const fm::TileShape& t, Geometry* g, int32_t* bn) {
-  *bn = t.bn_bwd;
-  int32_t st = check_layout(l, t.bm_bwd, t.bn_bwd, true, g);
-  if (st == FM_ERR_SHAPE && check_layout(l, t.bm_bwd, 2 * t.bn_bwd, true, g) == FM_OK) {
-    *bn = 2 * t.bn_bwd;
-    st = FM_OK;
+  if (l && l->nq < kLongQuery) {
+    *bn = t.bn_bwd;
+    const int32_t st = check_layout(l, t.bm_bwd, t.bn_bwd, true, g);
+    if (st != FM_ERR_SHAPE) return st;
   }
-  return st;
+  *bn = 2 * t.bn_bwd;
+  return check_layout(l, t.bm_bwd, 2 * t.bn_bwd, true, g);
 }
 
 size_t flashmask_bwd_ex_workspace_bytes(const fm_layout* l) {

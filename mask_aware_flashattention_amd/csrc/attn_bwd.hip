@@ -33,14 +33,19 @@ namespace fm {
 
 namespace {
 
-template <typename T, int D>
+// Two shapes of the kernel (NG key groups of 32 keys, a P wave and a dS wave each; NBUF tile
+// buffers):
+//   NG = 2, NBUF = 2: 4 waves per 64-key block, two workgroups per CU, which run independently of
+//     each other, and finer column lists (64-key blocks skip more fully masked tiles);
+//   NG = 4, NBUF = 3: 8 waves per 128-key block, one workgroup per CU, loads requested three
+//     units ahead: better where Q and dO no longer stay in the caches (long sequences), since
+//     each workgroup of the first shape loads the same Q/dO tiles for half as many keys.
+template <typename T, int D, int NG_, int NBUF_>
 struct BwdTile {
-  // NG key groups of 32 keys, a P wave and a dS wave each: 4 waves, and two workgroups per CU,
-  // which run independently of each other (better latency hiding than one 8-wave workgroup whose
-  // waves all meet at every barrier).
-  static constexpr int NG = 2;
+  static constexpr int NG = NG_, NBUF = NBUF_;
   static constexpr int BN = 32 * NG, BM = 64, NT = 128 * NG;
   static constexpr int BPW = 16 / NG, SPW = 4 / NG;  // per wave and tile: 1-KiB blocks, row slots
+  static constexpr int LPT = BPW + SPW;             // loads per wave and tile
   static constexpr int KPL = Elem<T>::KPL, KSTEP = 2 * KPL;
   static constexpr int CH = 16 / (int)sizeof(T);
   static constexpr int CPR = D / CH;  // 16-byte chunks per Q / dO / K row
@@ -65,28 +70,32 @@ struct MaskRegs {
 
 // GQ: more than one query head per key/value head (a.L.G > 1); the G = 1 instantiation walks a
 // single list and needs no guard for rows past nq.
-template <typename T, int D, bool GQ>
-__global__ __launch_bounds__(256, 2) void attn_bwd_kernel(BwdArgs a) {
-  using C = BwdTile<T, D>;
+template <typename T, int D, bool GQ, int NG, int NBUF>
+__global__ __launch_bounds__(128 * NG, sizeof(T) == 2 ? 4 / NG : 1) void attn_bwd_kernel(BwdArgs a) {
+  using C = BwdTile<T, D, NG, NBUF>;
   using E = Elem<T>;
   using frag = typename E::frag;
   constexpr int KPL = C::KPL, KSTEP = C::KSTEP, US = C::US;
 
-  // Two tile buffers, Q|dO|LSE2|D each, as separate arrays: the compiler then sees that the
-  // loads straight into one buffer never alias reads of the other and adds no waits for them.
-  // (Two workgroups of 76 KiB fit in a CU's LDS; three buffers would not.)
+  // NBUF tile buffers, Q|dO|LSE2|D each, as separate arrays: the compiler then sees that the
+  // loads straight into one buffer never alias reads of another and adds no waits for them.
+  // (Two workgroups of the 4-wave shape, 76 KiB each, fit in a CU's LDS.)
   __shared__ __attribute__((aligned(16))) unsigned char lds0[C::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char lds1[C::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char lds2[NBUF > 2 ? C::BUF_BYTES : 16];
   __shared__ __attribute__((aligned(16))) unsigned char xch[2 * C::XCH_BYTES];  // P of two units
   auto bufp = [&](auto bc) -> unsigned char* {
     constexpr int bi = decltype(bc)::value;
     if constexpr (bi == 0)
       return lds0;
-    else
+    else if constexpr (bi == 1)
       return lds1;
+    else
+      return lds2;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
@@ -94,25 +103,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(BwdArgs a) {
   const int kg = wv % C::NG;                                 // key group
   const bool dsw = wv >= C::NG;                              // the dS wave of the pair
 
-  // The workgroup owns BN keys of list key block kb of key/value head hk of batch b: the whole
-  // block, or for very long sequences (lists over 128-key blocks) one half of it, the two halves
-  // being neighbouring work items that walk the same list.  With G query heads per key/value
-  // head it walks the tile lists of all G heads in turn, accumulating into the same dK and dV
-  // registers (no atomics).
-  const int lbn = a.list_bn;
-  const int hshift = lbn > C::BN ? 1 : 0;  // log2 of the halves per list block
-  const int n_kb = (a.nk + lbn - 1) / lbn;
+  // The workgroup owns key block kb (BN keys) of key/value head hk of batch b; with G query heads
+  // per key/value head it walks the tile lists of all G heads in turn, accumulating into the
+  // same dK and dV registers (no atomics).
+  const int n_kb = (a.nk + C::BN - 1) / C::BN;
   const int work = xcd_contiguous_index(blockIdx.x, gridDim.x);
   // (every index here is the same for the whole workgroup; readfirstlane keeps it in scalar
   // registers, and with it every pointer and buffer descriptor derived from it)
   const int G = GQ ? a.L.G : 1;
   const int Hk = a.L.H / G;
-  const int bhk = __builtin_amdgcn_readfirstlane(work / (n_kb << hshift));
+  const int bhk = __builtin_amdgcn_readfirstlane(work / n_kb);
   const int b = __builtin_amdgcn_readfirstlane(bhk / Hk);
   const int hk = bhk - b * Hk, h0 = hk * G;
-  const int rem = work - bhk * (n_kb << hshift), half = rem & hshift;
-  const int kb = __builtin_amdgcn_readfirstlane(a.order[(size_t)mask_set(a.L, b, h0) * n_kb + (rem >> hshift)]);
-  const int key = kb * lbn + half * C::BN + kg * 32 + l32;  // this lane's key (a column of S)
+  const int kb = __builtin_amdgcn_readfirstlane(a.order[(size_t)mask_set(a.L, b, h0) * n_kb + work % n_kb]);
+  const int key = kb * C::BN + kg * 32 + l32;  // this lane's key (a column of S)
   const bool key_ok = key < a.nk;
   const int64_t kbase = b * a.L.ks_b + hk * a.L.ks_h;
   int total = 0;
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(BwdArgs a) {
     else
       bop[s] = __builtin_bit_cast(frag, buf_load4(kvbuf, off, 0));
   }
-  const bool ragged_block = (kb == n_kb - 1) && (a.nk % lbn) != 0;
+  const bool ragged_block = (kb == n_kb - 1) && (a.nk % C::BN) != 0;
 
   // ---- per-lane LDS byte offsets, constant for the whole kernel ------------------------------
   // Transpose-read lane geometry: lane i of 16-lane block b addresses row k0 + 8*(b/2) + i/4,
@@ -430,30 +434,46 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(BwdArgs a) {
   };
 
   // ---- the walk over the key block's query tiles ---------------------------------------------
-  // Tile t sits in buffer t % 2.  Right after the barrier of tile t's first unit, the loads of
-  // tile t+1 into the buffer tile t-1 used are issued (after that barrier no wave reads tile t-1:
-  // the dS wave finished its lagging unit of tile t-1 before it); before the barrier of tile t's
-  // second unit each wave waits for its loads, and that barrier publishes tile t+1.  A load so
-  // has one unit to land; the other workgroup on the CU covers the waits.
+  // Tile t sits in buffer t % NBUF.  Right after the barrier of tile t's first unit, the loads
+  // of tile t+NBUF-1 into the buffer tile t-1 used are issued (after that barrier no wave reads
+  // tile t-1: the dS wave finished its lagging unit of tile t-1 before it); before the barrier of
+  // tile t's second unit each wave waits until only the loads of tiles after t+1 are in flight,
+  // and that barrier publishes tile t+1.  A load so has 2*NBUF - 3 units to land (with two
+  // buffers the other workgroup on the CU covers the wait).  With three buffers every tile step
+  // issues exactly one tile's LPT loads (near the end a real tile is loaded again into a buffer
+  // nothing reads), so the wait needs no branch; a wait under a branch would make the compiler's
+  // own tracking assume the no-wait path and add vmcnt(0) before later reads.
   // The walk is written out once per role (same barriers in the same order), so that neither
   // role's loop carries the other's registers.
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
   {
     load_tile(first.gi, entry_of(first), I0{});
-    wait_vmem();
+    if constexpr (NBUF == 3) {
+      Cursor second = first;
+      if (total > 1) advance(second);
+      load_tile(second.gi, entry_of(second), I1{});  // tile 1, or tile 0 again (never read)
+      wait_vmem_n<C::LPT>();                         // tile 0 has landed
+    } else {
+      wait_vmem();
+    }
     lds_barrier();
   }
   f32x16 dp_prev = {};  // dS wave: dP of the pending unit
   auto walk = [&](auto role) {
-    Cursor cur = first;  // the tile being walked
+    Cursor cur = first;    // the tile being walked
+    Cursor ahead = first;  // the tile NBUF-1 ahead, loaded during this one
+    advance(ahead);
+    if (NBUF == 3 && total > 1) advance(ahead);
     int entry = entry_of(cur);
     frag op[C::QK_STEPS];
     read_ops(bufp(I0{}), 0, op);
-    // tile t in buffer bc = t % 2; tile t+1 goes into the other buffer, which tile t-1 used
+    // tile t in buffer bc = t % NBUF (a compile-time constant, so LDS offsets fold into the
+    // instructions); tile t+1 is in buffer (bc+1) % NBUF, tile t-1 was in (bc+NBUF-1) % NBUF
     auto tile = [&](const int t, auto bc) {
       constexpr int bi = decltype(bc)::value;
-      using BOther = std::integral_constant<int, bi ^ 1>;
+      using BNext = std::integral_constant<int, (bi + 1) % NBUF>;
+      using BPrev = std::integral_constant<int, (bi + NBUF - 1) % NBUF>;
       const bool test = (entry & 1) || ragged_block;
       uint64_t mrow = 0ull;  // the row test belongs to the P wave only
       if constexpr (!decltype(role)::value) {
@@ -464,27 +484,46 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(BwdArgs a) {
       }
       const unsigned char* qt = bufp(bc);
       const bool more = t + 1 < total;
-      Cursor nxt = cur;
-      if (more) advance(nxt);
+      const bool more_a = t + NBUF - 1 < total;  // the tile NBUF-1 ahead exists
       step(role, qt, H0{}, test, mrow, [&] {
         lds_barrier();
-        if (more) load_tile(nxt.gi, entry_of(nxt), BOther{});  // no wave reads tile t-1 now
-      }, op, dp_prev, true, qt, 1, bufp(BOther{}), t > 0);
+        if constexpr (NBUF == 3) {
+          load_tile(more_a ? ahead.gi : cur.gi, more_a ? entry_of(ahead) : entry, BPrev{});
+          if (more_a) advance(ahead);
+        } else if (more_a) {
+          load_tile(ahead.gi, entry_of(ahead), BPrev{});
+          advance(ahead);
+        }
+      }, op, dp_prev, true, qt, 1, bufp(BPrev{}), t > 0);
       step(role, qt, H1{}, test, mrow, [&] {
-        wait_vmem();    // this wave's part of tile t+1 has landed ...
+        // this wave's part of tile t+1 has landed ...
+        if constexpr (NBUF == 3)
+          wait_vmem_n<C::LPT>();
+        else
+          wait_vmem();
         lds_barrier();  // ... and everyone's
-      }, op, dp_prev, more, bufp(BOther{}), 0, qt, true);
+      }, op, dp_prev, more, bufp(BNext{}), 0, qt, true);
       if (more) {
-        cur = nxt;
+        advance(cur);
         entry = entry_of(cur);
       }
     };
     int t = 0;
-    for (; t + 1 < total; t += 2) {
-      tile(t, I0{});
-      tile(t + 1, I1{});
+    if constexpr (NBUF == 3) {
+      for (; t + 2 < total; t += 3) {
+        tile(t, I0{});
+        tile(t + 1, I1{});
+        tile(t + 2, I2{});
+      }
+      if (t < total) tile(t, I0{});
+      if (t + 1 < total) tile(t + 1, I1{});
+    } else {
+      for (; t + 1 < total; t += 2) {
+        tile(t, I0{});
+        tile(t + 1, I1{});
+      }
+      if (t < total) tile(t, I0{});
     }
-    if (t < total) tile(t, I0{});
   };
   if (dsw)
     walk(std::true_type{});
@@ -495,7 +534,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(BwdArgs a) {
   wait_vmem();
   // the dS wave's last pending unit: the second half of the last tile
   if (dsw) {
-    const unsigned char* ql = ((total - 1) & 1) ? lds1 : lds0;
+    const int lb = (total - 1) % NBUF;
+    const unsigned char* ql = lb == 0 ? lds0 : (lb == 1 ? lds1 : lds2);
     frag fr[US];
     ds_frags(1, dp_prev, fr);
     accumulate(ql, 1, fr);
@@ -523,17 +563,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_kernel(BwdArgs a) {
   }
 }
 
-template <typename T, int D>
-hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_end) {
-  using C = BwdTile<T, D>;
-  auto kernel = a.L.G > 1 ? &attn_bwd_kernel<T, D, true> : &attn_bwd_kernel<T, D, false>;
-  if (a.list_bn != C::BN && a.list_bn != 2 * C::BN) return hipErrorInvalidValue;
-  const int64_t n_kb = (a.nk + a.list_bn - 1) / a.list_bn;
-  const int64_t grid = (a.list_bn / C::BN) * n_kb * a.L.B * (a.L.H / a.L.G);
+template <typename T, int D, int NG, int NBUF>
+hipError_t run_shape(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_end) {
+  using C = BwdTile<T, D, NG, NBUF>;
+  auto kernel = a.L.G > 1 ? &attn_bwd_kernel<T, D, true, NG, NBUF> : &attn_bwd_kernel<T, D, false, NG, NBUF>;
+  const int64_t n_kb = (a.nk + C::BN - 1) / C::BN;
+  const int64_t grid = n_kb * a.L.B * (a.L.H / a.L.G);
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(C::NT), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (ev_end) (void)hipEventRecord(ev_end, stream);
   return err;
+}
+
+// The shape follows the width of the column lists' key blocks.
+template <typename T, int D>
+hipError_t run_bwd(const BwdArgs& a, hipStream_t stream, hipEvent_t ev_end) {
+  if (a.list_bn == BwdTile<T, D, 2, 2>::BN) return run_shape<T, D, 2, 2>(a, stream, ev_end);
+  if (a.list_bn == BwdTile<T, D, 4, 3>::BN) return run_shape<T, D, 4, 3>(a, stream, ev_end);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace

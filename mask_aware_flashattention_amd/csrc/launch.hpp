@@ -126,7 +126,7 @@ struct BwdArgs {
   const int32_t* klist;
   const int32_t* order;  // key blocks, longest list first
   int32_t list_stride;  // n_qb at the backward tile shape
-  int32_t list_bn;      // keys per key block of the lists: 64, or 128 for very long sequences
+  int32_t list_bn;      // keys per key block of the lists: 64, or 128 for long query sequences
   Layout L;
   int32_t nq, nk;
   float scale;
