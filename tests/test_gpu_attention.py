@@ -126,6 +126,6 @@ def test_forward_is_deterministic(fm):
 def test_every_walk_length(fm, tiles):
     """Without a mask every key block lists every query tile, so nq = 64*tiles - 5 gives the
     key-stationary walk exactly `tiles` tiles (the last one ragged): the tile pipeline's start,
-    its two-buffer rotation over an even or odd number of tiles, and both halves of a key block
-    (nk = 160: one full 128-key block and a ragged one)."""
+    its two-buffer rotation over an even or odd number of tiles, and both column groups of a key
+    block (nk = 160: two full 64-key blocks and a ragged one of 32 keys)."""
     run_case(fm, "bf16", 1, 1, 64 * tiles - 5, 160, "none", seed=tiles)
