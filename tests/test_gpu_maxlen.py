@@ -64,20 +64,23 @@ def test_max_length_sliding_window(fm):
         assert np.abs(rows_of(dv, j, j + 1) - dV).max() <= tol, j
 
 
-@pytest.mark.parametrize("w", [1, 64, 200, 300])
-def test_long_query_short_walks(fm, w):
+@pytest.mark.parametrize("dt,w", [("bf16", 1), ("bf16", 64), ("bf16", 200), ("bf16", 300),
+                                  ("fp32", 1), ("fp32", 200)])
+def test_long_query_short_walks(fm, dt, w):
     """nq >= 65536 selects the dK/dV kernel's 8-wave shape (128-key column blocks, three tile
     buffers); a sliding window of w keys gives every key block a walk of 2 to 7 query tiles, so
     the start of its pipeline, the three-buffer rotation and both remainders run at that shape.
-    nq = nk = 65536 + 77 leaves a ragged last block in both directions."""
+    nq = nk = 65536 + 77 leaves a ragged last block in both directions.  bf16 runs at d = 128,
+    float32 at d = 64."""
     n = 65536 + 77
+    d, dtype = (128, torch.bfloat16) if dt == "bf16" else (64, torch.float32)
     vec = masks.sliding_window(n, w)
     gv = [torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda() for x in vec]
     g = torch.Generator(device="cuda").manual_seed(w)
-    q, k, v, do = (torch.randn((1, 1, n, 128), generator=g, device="cuda").to(torch.bfloat16)
+    q, k, v, do = (torch.randn((1, 1, n, d), generator=g, device="cuda").to(dtype)
                    for _ in range(4))
-    scale = float(np.float32(1.0 / np.sqrt(128)))
-    print(f"long query, window {w}", flush=True)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    print(f"long query, {dt}, window {w}", flush=True)
     o, lse = fm.fwd(q, k, v, *gv, scale)
     dq, dk, dv = fm.bwd(q, k, v, o, do, lse, *gv, scale)
     torch.cuda.synchronize()
@@ -85,7 +88,7 @@ def test_long_query_short_walks(fm, w):
     def rows_of(t, a, b):
         return f64(t[0, 0, a:b])
 
-    tol = TOL["bf16"]
+    tol = TOL[dt]
     for i in (0, w, 4097, n // 2 + 3, n - 1):
         k0 = max(0, i - w + 1)
         sub = [x[k0:i + 1] for x in vec]
