@@ -19,6 +19,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -46,11 +47,19 @@ def unmasked_entries(vectors, nq: int) -> int:
     return int(nq * len(a1) - (l1 + l2 - ov).sum())
 
 
+def code_text(src: str) -> str:
+    """A kernel source without its comments, trailing blanks and empty lines: the text whose
+    change can change the kernel (the sources hold no string with a comment marker in it)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in src.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash(which: str = "bwd") -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[which]:
-        with open(os.path.join(ROOT, "mask_aware_flashattention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "mask_aware_flashattention_amd", "csrc", f)) as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -6,8 +6,9 @@
 // partly masked tiles, as the forward; "FlashMask-3 sends each GPU its mask ...",
 // tile-classification paragraph).
 //
-//   K5 dK / dV:  one workgroup of 4 waves per block of BN = 64 keys (two workgroups per CU):
-//                2 key groups of 32 keys, and per key group a pair of waves that split the work:
+//   K5 dK / dV:  one workgroup of 4 waves per block of BN = 64 keys (two workgroups per CU;
+//                queries of 65536 rows or more use 8 waves per 128 keys, one workgroup per CU):
+//                key groups of 32 keys, and per key group a pair of waves that split the work:
 //                  the P wave keeps K rows in registers, computes S = Q K^T, P = exp2(S*scale*
 //                  log2e - LSE*log2e) (0 where masked) and accumulates dV^T += dO^T P;
 //                  the dS wave keeps V rows, computes dP = dO V^T, takes P from the P wave
@@ -17,7 +18,8 @@
 //                the query blocks (BM = 64 rows) of its list in 32-row units; Q and dO rows
 //                are A operands read from LDS in a permuted row order so the accumulators
 //                double as operands, Q^T and dO^T come from the gfx950 LDS transpose read.
-//                Q/dO tiles go from HBM straight into two LDS buffers, requested a unit ahead;
+//                Q/dO tiles go from HBM straight into two LDS buffers (three in the 8-wave
+//                shape), each requested while the one before it (the two before it) compute;
 //                one workgroup barrier per unit (P handed over) also publishes the next tile,
 //                and these barriers wait only for LDS traffic, not for loads in flight.
 //   dQ comes from the query-stationary kernel in attn_bwd_dq.hip, so no float32 atomics are
@@ -37,8 +39,8 @@ namespace {
 // buffers):
 //   NG = 2, NBUF = 2: 4 waves per 64-key block, two workgroups per CU, which run independently of
 //     each other, and finer column lists (64-key blocks skip more fully masked tiles);
-//   NG = 4, NBUF = 3: 8 waves per 128-key block, one workgroup per CU, loads requested three
-//     units ahead: better where Q and dO no longer stay in the caches (long sequences), since
+//   NG = 4, NBUF = 3: 8 waves per 128-key block, one workgroup per CU, each tile requested two
+//     tiles ahead: better where Q and dO no longer stay in the caches (long sequences), since
 //     each workgroup of the first shape loads the same Q/dO tiles for half as many keys.
 template <typename T, int D, int NG_, int NBUF_>
 struct BwdTile {

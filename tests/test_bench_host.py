@@ -33,3 +33,12 @@ def test_more_than_one_gpu_refused():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
                        text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_source_hash_ignores_comments_only():
+    """The counter records are tied to the kernels' code, not to their comments."""
+    src = "int f(int x) {  // add one\n  /* block\n comment */\n  return x + 1;\n}\n"
+    same = "// header\nint f(int x) {\n\n  return x + 1;   // other words\n}\n"
+    other = "int f(int x) {\n  return x + 2;\n}\n"
+    assert bench.code_text(src) == bench.code_text(same)
+    assert bench.code_text(src) != bench.code_text(other)
