@@ -3,9 +3,11 @@ float64 oracle: random batch and head counts, grouped key/value heads (G = 1..3)
 1..419 (square shapes also draw the structured mask families), both built dtypes.  Each case is
 its own test so a failure names its seed.  Bars as elsewhere: O, dQ within 2e-2 (bf16) or 1e-4
 (fp32), LSE within 1e-3 with identical -inf rows, and a grouped dK / dV (a sum of G per-head
-gradients) within G times the bar."""
+gradients) within G times the bar.  FM_RANDOM_CASES sets the number of cases (default 24); the
+first cases of a longer sweep are the default ones."""
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -49,7 +51,7 @@ def draw(case):
     return dtype, B, Hkv, G, nq, nk, kind, v
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(int(os.environ.get("FM_RANDOM_CASES", "24"))))
 def test_random_shape(fm, case):
     dtype, B, Hkv, G, nq, nk, kind, v = draw(case)
     H = Hkv * G
