@@ -132,10 +132,14 @@ int32_t flashmask_bwd(const fm_shape* shape, const void* Q, const void* K, const
  *                           (mask_b > 1 ? b : 0) * mask_h + (mask_h > 1 ? h : 0).
  *                           mask_b is 1 or B, mask_h is 1 or H.
  * Requirements (FM_ERR_SHAPE unless noted): strides >= 0, row strides >= d, every row
- * start 16-byte aligned (stride * element size a multiple of 16, FM_ERR_ALIGN); per batch and
- * head the rows span less than 4 GiB: (nq-1)*q_stride[2] + d elements (and for the backward
- * also (H/H_kv - 1)*q_stride[1] more, with H/H_kv <= 256), (nk-1)*kv_stride[2] + d elements.
- * Distinct outputs must not overlap each other or the inputs (not checked).  LSE stays
+ * start 16-byte aligned (stride * element size a multiple of 16, FM_ERR_ALIGN); no two
+ * (batch, head, row) positions of one layout share memory (sorted by stride, every axis with
+ * more than one entry steps over the span of the smaller axes, so a zero batch or head stride
+ * is rejected when B or H is above 1: outputs are written through these strides); per batch
+ * and head the rows, counted up to the next multiple of 128 (the kernels address whole tiles),
+ * span less than 4 GiB: (ceil(nq/128)*128 - 1)*q_stride[2] + d elements (and for the backward
+ * also (H/H_kv - 1)*q_stride[1] more, with H/H_kv <= 256), (ceil(nk/128)*128 - 1)*kv_stride[2]
+ * + d elements.  Distinct tensors must not overlap each other (not checked).  LSE stays
  * contiguous float32 [B][H][nq].  In the backward dK and dV of a key/value head sum the
  * gradients of its H/H_kv query heads, still without atomics and deterministic.
  * Workspaces grow with the number of mask sets (lists per set).
@@ -244,9 +248,9 @@ int32_t flashmask_block_order(const int32_t* cnt, int32_t n, int32_t* order, voi
  * library).  After this call, flashmask_fwd records fwd_begin / fwd_end and flashmask_bwd
  * records bwd_begin / bwd_end (hipEvent_t passed as void*, created by the caller) on the call's
  * stream immediately before and after its attention kernels (for the backward: before the dQ
- * kernel and after the dK/dV kernel, which runs second).  NULL disables a pair.  This is the
- * library's only state: process-wide, not synchronised; set it from the thread that makes the
- * calls.
+ * kernel and after the dK/dV kernel, which runs second).  NULL disables a pair.  The events
+ * are kept per calling thread (thread-local): they apply only to later calls from the same
+ * thread, so other threads' calls never record into them.  This is the library's only state.
  */
 int32_t flashmask_set_profile_events(void* fwd_begin, void* fwd_end, void* bwd_begin,
                                      void* bwd_end);

@@ -26,9 +26,12 @@ def _stream(device):
 
 
 def _require_cuda(*ts):
+    dev = ts[0].device
     for t in ts:
         if not t.is_cuda:
             raise ValueError("tensors must be on a ROCm/CUDA device")
+        if t.device != dev:
+            raise ValueError("tensors must be on one device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
 
@@ -40,15 +43,36 @@ def _vectors(lts, lte, uts, ute, nk):
     _require_cuda(lts, lte, uts, ute)
 
 
-def _shape(q, k):
-    if q.dim() != 4 or k.dim() != 4:
+def _expect(t, name, shape, dtype):
+    """t must have exactly this shape and dtype (checked before any pointer is passed on: the C
+    interface sees no tensor sizes, so a short or mistyped buffer would be read or written out
+    of bounds)."""
+    if t is None:
+        raise ValueError(f"{name} is missing")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _shape(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q must be [B, H, nq, d] and k, v [B, H, nk, d]")
     B, H, nq, d = q.shape
     if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
-        raise ValueError("q and k/v disagree on B, H or d")
+        raise ValueError("q and k disagree on B, H or d")
     if q.dtype not in _DTYPES:
         raise ValueError("dtype must be bfloat16 or float32")
+    _expect(k, "k", k.shape, q.dtype)
+    _expect(v, "v", k.shape, q.dtype)
     return FmShape(B, H, nq, k.shape[2], d, _DTYPES[q.dtype])
+
+
+def _check_workspace(ws, device):
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    if ws.device != device:
+        raise ValueError("workspace must be on the tensors' device")
 
 
 def tile_sizes(dtype=torch.bfloat16, d: int = 128):
@@ -75,14 +99,19 @@ def fwd(q, k, v, lts, lte, uts, ute, scale=None, *, out=None, lse=None, workspac
     """O, LSE = masked attention forward.  q [B,H,nq,d], k/v [B,H,nk,d] (bf16 d=128 or fp32
     d=64), mask vectors int32 [nk].  Returns (O like q, LSE float32 [B,H,nq])."""
     lib = _lib.load()
-    shape = _shape(q, k)
-    _require_cuda(q, k, v)
+    shape = _shape(q, k, v)
+    if out is not None:
+        _expect(out, "out", q.shape, q.dtype)
+    if lse is not None:
+        _expect(lse, "lse", q.shape[:3], torch.float32)
+    _require_cuda(q, k, v, *[t for t in (out, lse) if t is not None])
     _vectors(lts, lte, uts, ute, shape.nk)
     if scale is None:
         scale = 1.0 / math.sqrt(shape.d)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     ws = workspace if workspace is not None else _workspace(fwd_workspace_bytes(shape), q.device)
+    _check_workspace(ws, q.device)
     st = lib.flashmask_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lts), _ptr(lte),
                            _ptr(uts), _ptr(ute), ctypes.c_float(scale), _ptr(o), _ptr(lse_t),
                            _ptr(ws), ws.numel(), _stream(q.device))
@@ -93,16 +122,23 @@ def fwd(q, k, v, lts, lte, uts, ute, scale=None, *, out=None, lse=None, workspac
 def bwd(q, k, v, o, do, lse, lts, lte, uts, ute, scale=None, *, workspace=None, grads=None):
     """dQ, dK, dV of L = sum(O * dO).  ``o`` and ``lse`` are the forward's outputs."""
     lib = _lib.load()
-    shape = _shape(q, k)
-    _require_cuda(q, k, v, o, do, lse)
-    _vectors(lts, lte, uts, ute, shape.nk)
-    if scale is None:
-        scale = 1.0 / math.sqrt(shape.d)
+    shape = _shape(q, k, v)
+    _expect(o, "o", q.shape, q.dtype)
+    _expect(do, "do", q.shape, q.dtype)
+    _expect(lse, "lse", q.shape[:3], torch.float32)
     if grads is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = grads
+        _expect(dq, "dq", q.shape, q.dtype)
+        _expect(dk, "dk", k.shape, q.dtype)
+        _expect(dv, "dv", k.shape, q.dtype)
+    _require_cuda(q, k, v, o, do, lse, dq, dk, dv)
+    _vectors(lts, lte, uts, ute, shape.nk)
+    if scale is None:
+        scale = 1.0 / math.sqrt(shape.d)
     ws = workspace if workspace is not None else _workspace(bwd_workspace_bytes(shape), q.device)
+    _check_workspace(ws, q.device)
     st = lib.flashmask_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
                            _ptr(lse), _ptr(lts), _ptr(lte), _ptr(uts), _ptr(ute),
                            ctypes.c_float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
@@ -125,6 +161,10 @@ def _layout(q, k, v, vec):
         raise ValueError("dtype must be bfloat16 or float32, the same for q, k, v")
     if q.stride(3) != 1 or k.stride(3) != 1:
         raise ValueError("the d axis must be contiguous")
+    _no_overlap(q, "q")
+    _no_overlap(k, "k")
+    if q.device != k.device or q.device != v.device or not q.is_cuda:
+        raise ValueError("q, k, v must be on one ROCm/CUDA device")
     if vec.dim() == 1:
         mb, mh = 1, 1
     elif vec.dim() == 2:
@@ -140,6 +180,22 @@ def _layout(q, k, v, vec):
         lay.q_stride[i] = q.stride(i)
         lay.kv_stride[i] = k.stride(i)
     return lay
+
+
+def _no_overlap(t, name):
+    """No two (batch, head, row) positions of t's layout may share memory: outputs are created
+    with (and written through) the same strides, so a zero batch or head stride (an expanded
+    view) or interleaved heads would make workgroups write the same bytes."""
+    B, H, n, d = t.shape
+    span = d
+    for extent, stride in sorted(((B, t.stride(0)), (H, t.stride(1)), (n, t.stride(2))),
+                                 key=lambda x: x[1]):
+        if extent <= 1:
+            continue
+        if stride < span:
+            raise ValueError(f"{name}: batch, head and row strides {t.stride()[:3]} overlap "
+                             f"(an expanded or interleaved view); pass a copy")
+        span = (extent - 1) * stride + span
 
 
 def _vector_sets(lts, lte, uts, ute, nk):
@@ -165,11 +221,18 @@ def fwd_ex(q, k, v, lts, lte, uts, ute, scale=None, *, out=None, lse=None, works
     if scale is None:
         scale = 1.0 / math.sqrt(lay.d)
     o = _like_strided(None, q) if out is None else out
-    if o.stride() != q.stride():
-        raise ValueError("out must have q's strides")
+    _expect(o, "out", q.shape, q.dtype)
+    if o.stride() != q.stride() or o.device != q.device:
+        raise ValueError("out must have q's strides and device")
+    if lse is not None:
+        _expect(lse, "lse", q.shape[:3], torch.float32)
+        _require_cuda(lse)
+        if lse.device != q.device:
+            raise ValueError("lse must be on q's device")
     lse_t = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if lse is None else lse
     nbytes = lib.flashmask_fwd_ex_workspace_bytes(ctypes.byref(lay))
     ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    _check_workspace(ws, q.device)
     st = lib.flashmask_fwd_ex(ctypes.byref(lay), _ptr(q), _ptr(k), _ptr(v), _ptr(lts), _ptr(lte),
                               _ptr(uts), _ptr(ute), ctypes.c_float(scale), _ptr(o), _ptr(lse_t),
                               _ptr(ws), ws.numel(), _stream(q.device))
@@ -183,13 +246,20 @@ def bwd_ex(q, k, v, o, do, lse, lts, lte, uts, ute, scale=None, *, workspace=Non
     lib = _lib.load()
     lay = _layout(q, k, v, lts)
     _vector_sets(lts, lte, uts, ute, lay.nk)
+    _expect(o, "o", q.shape, q.dtype)
+    _expect(do, "do", q.shape, q.dtype)
+    _expect(lse, "lse", q.shape[:3], torch.float32)
     if o.stride() != q.stride() or do.stride() != q.stride():
         raise ValueError("o and do must have q's strides")
+    _require_cuda(lse)
+    if o.device != q.device or do.device != q.device or lse.device != q.device:
+        raise ValueError("o, do and lse must be on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(lay.d)
     dq, dk, dv = _like_strided(None, q), _like_strided(None, k), _like_strided(None, v)
     nbytes = lib.flashmask_bwd_ex_workspace_bytes(ctypes.byref(lay))
     ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    _check_workspace(ws, q.device)
     st = lib.flashmask_bwd_ex(ctypes.byref(lay), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
                               _ptr(lse), _ptr(lts), _ptr(lte), _ptr(uts), _ptr(ute),
                               ctypes.c_float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),

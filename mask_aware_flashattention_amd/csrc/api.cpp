@@ -75,6 +75,33 @@ fm::Layout to_internal(const fm_layout* l) {
 
 inline int32_t mask_sets(const fm_layout* l) { return l->mask_b * l->mask_h; }
 
+// Rows of the largest tile any attention kernel reads at once (query blocks of the forward and
+// dQ kernels, key blocks of the dK/dV kernel's 8-wave shape).
+constexpr int64_t kPadRows = 128;
+
+// True if the (batch, head, row) element offsets of a [B][H][n][d] view with these element
+// strides (d contiguous) never coincide: sorted by stride, each axis of extent > 1 must step
+// over everything the smaller axes span.  A zero stride on an axis of extent > 1 fails.
+bool non_overlapping(int64_t B, int64_t H, int64_t n, int64_t d, const int64_t* stride) {
+  struct Ax {
+    int64_t extent, stride;
+  } ax[3] = {{B, stride[0]}, {H, stride[1]}, {n, stride[2]}};
+  // insertion sort by stride (three entries)
+  for (int i = 1; i < 3; ++i)
+    for (int j = i; j > 0 && ax[j].stride < ax[j - 1].stride; --j) {
+      const Ax t = ax[j];
+      ax[j] = ax[j - 1];
+      ax[j - 1] = t;
+    }
+  int64_t span = d;  // elements spanned by the axes below (a row is d contiguous elements)
+  for (int i = 0; i < 3; ++i) {
+    if (ax[i].extent <= 1) continue;
+    if (ax[i].stride < span) return false;
+    span = (ax[i].extent - 1) * ax[i].stride + span;
+  }
+  return true;
+}
+
 // Layout checks shared by forward and backward (bwd: the dK/dV kernel also spans the query
 // heads of a group); fills the tile geometry for (BM, BN).
 int32_t check_layout(const fm_layout* l, int32_t BM, int32_t BN, bool bwd, Geometry* g) {
@@ -98,14 +125,24 @@ int32_t check_layout(const fm_layout* l, int32_t BM, int32_t BN, bool bwd, Geome
   if (l->q_stride[2] < l->d || l->kv_stride[2] < l->d) return FM_ERR_SHAPE;
   for (int i = 0; i < 3; ++i)
     if ((l->q_stride[i] * es) % 16 != 0 || (l->kv_stride[i] * es) % 16 != 0) return FM_ERR_ALIGN;
-  // Every buffer a kernel addresses with 32-bit offsets stays below 4 GiB.
+  // O and dQ are written through q_stride, dK and dV through kv_stride: distinct (batch, head,
+  // row) must reach distinct memory.
+  if (!non_overlapping(l->B, l->H, l->nq, l->d, l->q_stride) ||
+      !non_overlapping(l->B, l->H_kv, l->nk, l->d, l->kv_stride))
+    return FM_ERR_SHAPE;
+  // Every buffer a kernel addresses with 32-bit offsets stays below 4 GiB, including the rows
+  // past the end that the last (ragged) tile addresses: the kernels read whole tiles of up to
+  // kPadRows rows and rely on such offsets landing past the buffer's end (where loads return
+  // zeros), so they must not wrap around 2^32.
   const int64_t G = l->H / l->H_kv;
-  int64_t q_span = ((int64_t)(l->nq - 1) * l->q_stride[2] + l->d) * es;
+  const int64_t nq_pad = ceil_div(l->nq, kPadRows) * kPadRows;
+  const int64_t nk_pad = ceil_div(l->nk, kPadRows) * kPadRows;
+  int64_t q_span = ((nq_pad - 1) * l->q_stride[2] + l->d) * es;
   if (bwd) {
     if (G > 256) return FM_ERR_SHAPE;
     q_span += (G - 1) * l->q_stride[1] * es;
   }
-  const int64_t k_span = ((int64_t)(l->nk - 1) * l->kv_stride[2] + l->d) * es;
+  const int64_t k_span = ((nk_pad - 1) * l->kv_stride[2] + l->d) * es;
   if (q_span >= (int64_t(1) << 32) || k_span >= (int64_t(1) << 32)) return FM_ERR_SHAPE;
   if (g) *g = Geometry{n_qb, n_kb};
   return FM_OK;
@@ -152,7 +189,9 @@ BwdWs bwd_layout(const fm_layout* s, const Geometry& g, const Geometry& gf) {
 inline int32_t hip_status(hipError_t e) { return e == hipSuccess ? FM_OK : FM_ERR_HIP; }
 
 // Optional timing events (flashmask_set_profile_events); null unless a benchmark sets them.
-hipEvent_t g_fwd_begin = nullptr, g_fwd_end = nullptr, g_bwd_begin = nullptr, g_bwd_end = nullptr;
+// Per calling thread, so calls made from other threads never record into them.
+thread_local hipEvent_t g_fwd_begin = nullptr, g_fwd_end = nullptr, g_bwd_begin = nullptr,
+                        g_bwd_end = nullptr;
 
 }  // namespace
 

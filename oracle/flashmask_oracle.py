@@ -216,8 +216,8 @@ def _run_jobs(fn, jobs, workers):
 
 def block_minmax(vec, BN: int):
     """Per key block b (keys [b*BN, min((b+1)*BN, nk))): the minimum and the maximum of the
-    vector over that block only ([explainer, tile-classification paragraph]: "the maximum and
-    minimum along the key axis").  Returns (mins, maxs) as int64 arrays of length ceil(nk/BN)."""
+    vector over that block only (the explainer's tile-classification paragraph reduces each
+    vector to its extremes over the keys of a block).  Returns (mins, maxs) as int64 arrays of length ceil(nk/BN)."""
     v = np.asarray(vec, dtype=np.int64)
     nk = v.shape[0]
     n_kb = -(-nk // BN)

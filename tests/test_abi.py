@@ -270,6 +270,24 @@ def test_ex_layout_checks(lib):
     ]
     for kw in shape_errors:
         assert fwd_ex(lib, layout(**kw)) == FM_ERR_SHAPE, kw
+    # outputs are written through the same strides: no two (batch, head, row) may share memory
+    overlap = [
+        dict(H=2, qs=(2 * 300 * 128, 0, 128)),            # zero head stride, two heads
+        dict(B=2, qs=(0, 300 * 128, 128)),                # zero batch stride, two batches
+        dict(H=2, qs=(2 * 300 * 128, 128 * 100, 128)),    # head 1 starts inside head 0's rows
+        dict(H=2, H_kv=2, ks=(2 * 200 * 128, 64, 256)),   # heads interleave with a half row
+    ]
+    for kw in overlap:
+        assert fwd_ex(lib, layout(**kw)) == FM_ERR_SHAPE, kw
+        assert bwd_ex(lib, layout(**kw)) == FM_ERR_SHAPE, kw
+    # packed [B, n, 3, H, d] projections: heads interleave inside a row without overlapping
+    assert fwd_ex(lib, layout(B=2, H=4, qs=(300 * 3 * 4 * 128, 128, 3 * 4 * 128),
+                              ks=(200 * 3 * 4 * 128, 128, 3 * 4 * 128))) == FM_ERR_WORKSPACE
+    # the rows of the ragged last 128-row tile are addressed too: nq = 1365 rows of 3 MiB end
+    # below 4 GiB, but 1408 (the next multiple of 128) do not
+    wide = 3 * (1 << 19)
+    assert fwd_ex(lib, layout(H=1, nq=1365, qs=(1365 * wide, 1365 * wide, wide))) == FM_ERR_SHAPE
+    assert fwd_ex(lib, layout(H=1, nq=1280, qs=(1280 * wide, 1280 * wide, wide))) == FM_ERR_WORKSPACE
     # every row start 16-byte aligned: strides * 2 bytes must be multiples of 16
     assert fwd_ex(lib, layout(qs=(2 * 300 * 128, 300 * 128 + 4, 128))) == FM_ERR_ALIGN
     assert fwd_ex(lib, layout(ks=(2 * 200 * 128, 200 * 128, 132))) == FM_ERR_ALIGN
