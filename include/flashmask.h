@@ -47,7 +47,9 @@ typedef enum {
   FM_ERR_WORKSPACE = 6,   /* workspace smaller than the *_workspace_bytes value, or NULL      */
   FM_ERR_CHUNKS = 7,      /* chunk table not sorted / disjoint / non-empty / inside range     */
   FM_ERR_HIP = 8,         /* a HIP launch failed                                              */
-  FM_ERR_VALUE = 9        /* a scalar argument is invalid (scale not finite and positive)    */
+  FM_ERR_VALUE = 9,       /* a scalar argument is invalid (scale not finite and positive)    */
+  FM_ERR_SCRATCH = 10     /* the problem needs more workspace than a no-alloc call's fixed
+                             scratch array holds                                             */
 } fm_status;
 
 typedef enum { FM_BF16 = 0, FM_FP32 = 1 } fm_dtype;
@@ -242,6 +244,24 @@ int32_t flashmask_prune_chunks(const int32_t* LTS, const int32_t* LTE, const int
  * FM_ERR_ALIGN, FM_ERR_HIP.
  */
 int32_t flashmask_block_order(const int32_t* cnt, int32_t n, int32_t* order, void* stream);
+
+/*
+ * Forward attention that allocates nothing and takes no workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, kernels and results as flashmask_fwd without ws/ws_bytes:
+ * the workspace is a fixed device array inside the library of
+ * flashmask_fwd_noalloc_max_workspace_bytes() = 16 MiB per GPU (held until the process ends;
+ * its device address is looked up once per device, on the first call made with that device
+ * current).  A problem whose flashmask_fwd_workspace_bytes exceeds it returns FM_ERR_SCRATCH
+ * before any device work (one mask set at nq = nk = 131072 needs 8.1 MiB).  Every call on a GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must not be made.  No hipMalloc, hipFree or allocating library routine is
+ * called.
+ */
+size_t flashmask_fwd_noalloc_max_workspace_bytes(void);
+int32_t flashmask_fwd_noalloc(const fm_shape* shape, const void* Q, const void* K, const void* V,
+                              const int32_t* LTS, const int32_t* LTE, const int32_t* UTS,
+                              const int32_t* UTE, float scale, void* O, float* LSE, void* stream);
 
 /*
  * Diagnostic hook for timing the attention kernels alone (a benchmark aid; not needed to use the

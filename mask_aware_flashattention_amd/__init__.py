@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     classify,
     fwd,
     fwd_ex,
+    fwd_noalloc,
     fwd_workspace_bytes,
     localize,
     prune_chunks,

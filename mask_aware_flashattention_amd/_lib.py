@@ -55,6 +55,9 @@ SIGNATURES = {
     "flashmask_fwd_ex_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FmLayout)]),
     "flashmask_fwd_ex": (c_i32, [ctypes.POINTER(FmLayout), c_p, c_p, c_p, c_p, c_p, c_p, c_p,
                                  ctypes.c_float, c_p, c_p, c_p, ctypes.c_size_t, c_p]),
+    "flashmask_fwd_noalloc_max_workspace_bytes": (ctypes.c_size_t, []),
+    "flashmask_fwd_noalloc": (c_i32, [ctypes.POINTER(FmShape), c_p, c_p, c_p, c_p, c_p, c_p, c_p,
+                                      ctypes.c_float, c_p, c_p, c_p]),
     "flashmask_bwd_ex_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FmLayout)]),
     "flashmask_bwd_ex": (c_i32, [ctypes.POINTER(FmLayout), c_p, c_p, c_p, c_p, c_p, c_p, c_p,
                                  c_p, c_p, c_p, ctypes.c_float, c_p, c_p, c_p, c_p,

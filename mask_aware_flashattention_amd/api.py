@@ -119,6 +119,25 @@ def fwd(q, k, v, lts, lte, uts, ute, scale=None, *, out=None, lse=None, workspac
     return o, lse_t
 
 
+def fwd_noalloc(q, k, v, lts, lte, uts, ute, scale=None, *, out, lse):
+    """The forward without a workspace (flashmask_fwd_noalloc): the library's fixed 16 MiB
+    device array stands in for it, so nothing is allocated here either; out and lse must be
+    given.  Calls that overlap in time on one GPU race on that array."""
+    lib = _lib.load()
+    shape = _shape(q, k, v)
+    _expect(out, "out", q.shape, q.dtype)
+    _expect(lse, "lse", q.shape[:3], torch.float32)
+    _require_cuda(q, k, v, out, lse)
+    _vectors(lts, lte, uts, ute, shape.nk)
+    if scale is None:
+        scale = 1.0 / math.sqrt(shape.d)
+    st = lib.flashmask_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lts),
+                                   _ptr(lte), _ptr(uts), _ptr(ute), ctypes.c_float(scale),
+                                   _ptr(out), _ptr(lse), _stream(q.device))
+    check(st, "flashmask_fwd_noalloc")
+    return out, lse
+
+
 def bwd(q, k, v, o, do, lse, lts, lte, uts, ute, scale=None, *, workspace=None, grads=None):
     """dQ, dK, dV of L = sum(O * dO).  ``o`` and ``lse`` are the forward's outputs."""
     lib = _lib.load()

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libflashmask.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "mask_kernels.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip"]
+SOURCES = ["api.cpp", "mask_kernels.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_dq.hip",
+           "noalloc.hip"]
 # Per-source code-generation options (none at present).
 EXTRA = {}
 ARCH = "gfx950"

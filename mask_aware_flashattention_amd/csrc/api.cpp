@@ -209,6 +209,7 @@ const char* flashmask_strerror(int32_t status) {
     case FM_ERR_CHUNKS: return "chunk table not sorted, disjoint, non-empty and in range (1..64 chunks)";
     case FM_ERR_HIP: return "HIP launch failed";
     case FM_ERR_VALUE: return "invalid scalar argument (scale must be finite and > 0)";
+    case FM_ERR_SCRATCH: return "problem too large for the no-alloc call's fixed scratch array";
     default: return "unknown status";
   }
 }

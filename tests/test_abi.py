@@ -17,6 +17,7 @@ HEADER = os.path.join(ROOT, "include", "flashmask.h")
 
 FM_OK, FM_ERR_NULL, FM_ERR_SHAPE, FM_ERR_DTYPE, FM_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 FM_ERR_ALIGN, FM_ERR_WORKSPACE, FM_ERR_CHUNKS, FM_ERR_HIP, FM_ERR_VALUE = 5, 6, 7, 8, 9
+FM_ERR_SCRATCH = 10
 
 P = ctypes.c_void_p(0x100000)       # fake, 256-byte aligned "device" address (never touched)
 P2 = ctypes.c_void_p(0x200000)
@@ -40,14 +41,14 @@ def declared_functions():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
 
 
 def test_strerror(lib):
-    for s in range(10):
+    for s in range(11):
         assert lib.flashmask_strerror(s)
     assert b"unknown" in lib.flashmask_strerror(1234)
 
@@ -310,3 +311,18 @@ def test_bwd_ex_checks(lib):
     assert bwd_ex(lib, layout(), dk=NUL) == FM_ERR_NULL
     assert bwd_ex(lib, layout(), dk=MIS) == FM_ERR_ALIGN
     assert bwd_ex(lib, layout(), scale=0.0) == FM_ERR_VALUE
+
+
+def test_noalloc_checks(lib):
+    """The no-alloc forward refuses a problem larger than its fixed array, and otherwise runs
+    the forward's own argument checks, all before any device work."""
+    assert lib.flashmask_fwd_noalloc_max_workspace_bytes() == 16 << 20
+
+    def call(s, q=P, scale=0.1):
+        return lib.flashmask_fwd_noalloc(ctypes.byref(s) if s is not None else None, q, P, P, P,
+                                         P, P, P, ctypes.c_float(scale), P2, P2, NUL)
+    assert call(None) == FM_ERR_NULL
+    assert call(shape(nq=1 << 18, nk=1 << 18, H=1)) == FM_ERR_SCRATCH   # 32 MiB of lists
+    assert call(shape(d=64)) == FM_ERR_UNSUPPORTED
+    assert call(shape(nq=0)) == FM_ERR_SHAPE
+    assert call(shape(), q=NUL) == FM_ERR_NULL   # before the device is touched
