@@ -10,6 +10,8 @@ for a set of key columns only the rows with an unmasked entry in those columns c
 from __future__ import annotations
 
 import os
+import threading
+from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
 
 import numpy as np
 import torch
@@ -60,6 +62,63 @@ def cols_reference(q, k, v, do, vectors, cols, mask_rows_all, scale):
     pos = np.searchsorted(keys, cols)
     _, dk, dv = oracle.bwd_rows(q[R], k[keys], v[keys], do[R], M[:, keys], scale, cols=pos)
     return dk, dv
+
+
+def oracle_workers():
+    """Worker threads for the whole-head oracle: the host's cores, at most 16 (a GPU machine's share
+    of its host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def whole_head_reference(q, k, v, do, vectors, mask_rows, scale, row_block=128, workers=None):
+    """O, LSE, dQ (every query row) and dK, dV (every key column) of one (batch, head), in float64.
+
+    The oracle's own row functions run on exact sub-problems: for each block of ``row_block``
+    consecutive query rows only the keys that are unmasked for at least one of those rows take
+    part (every other key is masked for all of them, so it has probability exactly zero and adds
+    nothing to any sum).  Each block's dQ is complete; its dK / dV contributions at those keys
+    are summed over the blocks.  Blocks run on a thread pool (numpy and BLAS release the GIL;
+    BLAS at one thread per worker), at most 2 x workers blocks in flight so memory stays
+    bounded.  q, do: [nq, d]; k, v: [nk, d] (float64 arrays); mask_rows: mask-row number of each
+    query row (global numbering for a context-parallel share)."""
+    from threadpoolctl import threadpool_limits
+
+    nq, d = q.shape
+    nk = k.shape[0]
+    mask_rows = np.asarray(mask_rows)
+    O = np.zeros((nq, v.shape[1]))
+    LSE = np.full(nq, -np.inf)
+    dQ = np.zeros((nq, d))
+    dK = np.zeros((nk, d))
+    dV = np.zeros((nk, v.shape[1]))
+    lock = threading.Lock()
+
+    def block(r0):
+        r1 = min(nq, r0 + row_block)
+        M = oracle.dense_mask(*vectors, mask_rows[r0:r1])
+        keys = np.flatnonzero(~M.all(axis=0))
+        if keys.size == 0:
+            return  # every row fully masked: O = 0, LSE = -inf, no gradient anywhere
+        Ms = M[:, keys]
+        o, lse = oracle.fwd_rows(q[r0:r1], k[keys], v[keys], Ms, scale)
+        dq, dk, dv = oracle.bwd_rows(q[r0:r1], k[keys], v[keys], do[r0:r1], Ms, scale)
+        O[r0:r1], LSE[r0:r1], dQ[r0:r1] = o, lse, dq
+        with lock:
+            dK[keys] += dk
+            dV[keys] += dv
+
+    workers = workers or oracle_workers()
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as ex:
+        pending = set()
+        for r0 in range(0, nq, row_block):
+            if len(pending) >= 2 * workers:
+                done, pending = wait(pending, return_when=FIRST_COMPLETED)
+                for f in done:
+                    f.result()
+            pending.add(ex.submit(block, r0))
+        for f in pending:
+            f.result()
+    return O, LSE, dQ, dK, dV
 
 
 def column_cost(vectors, col, mask_rows_all):

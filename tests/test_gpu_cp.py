@@ -12,6 +12,9 @@ share run one after another and put back together.
   result are round-to-nearest bf16 of float32 sums, so the reassembled sum may differ from the
   global dK by at most 2^-8 (sum of |partials| + |global|) plus float32 reordering (bound used
   below).  Chunks that the prune list drops contribute nothing to a rank.
+  The reassembled result of head 0 (O, LSE, dQ put back at the ranks' rows; dK and dV summed
+  over the ranks) is also compared element by element with the float64 oracle of the global
+  problem, every row and every key column.
 """
 
 import numpy as np
@@ -19,7 +22,7 @@ import pytest
 import torch
 
 import oracle
-from tests.parity import dev_i32
+from tests.parity import TOL, assert_close, assert_lse, dev_i32, f64, whole_head_reference
 from workloads import configs, masks
 
 pytestmark = pytest.mark.gpu
@@ -83,6 +86,9 @@ def test_all_ranks_reassemble_to_the_global_call(fm, global_vectors):
     o, lse = fm.fwd(q, k, v, *gv)
     dq, dk, dv = fm.bwd(q, k, v, o, do, lse, *gv)
 
+    o_re = torch.zeros_like(o[0, 0])     # head 0 put back together from the ranks
+    lse_re = torch.full_like(lse[0, 0], float("nan"))
+    dq_re = torch.zeros_like(dq[0, 0])
     dk_sum = torch.zeros_like(dk, dtype=torch.float32)
     dv_sum = torch.zeros_like(dv, dtype=torch.float32)
     dk_abs = torch.zeros_like(dk_sum)
@@ -101,6 +107,9 @@ def test_all_ranks_reassemble_to_the_global_call(fm, global_vectors):
         assert torch.equal(o_l, o.index_select(2, rows)), r
         assert torch.equal(lse_l, lse.index_select(2, rows)), r
         assert torch.equal(dq_l, dq.index_select(2, rows)), r
+        o_re[rows] = o_l[0, 0]
+        lse_re[rows] = lse_l[0, 0]
+        dq_re[rows] = dq_l[0, 0]
         # keys of chunks the rank prunes get exactly zero gradient from it
         live = fm.prune_chunks(*lv[:4], lv[4], CHUNK, CHUNK)
         dead = torch.nonzero(live == 0).flatten()
@@ -117,3 +126,14 @@ def test_all_ranks_reassemble_to_the_global_call(fm, global_vectors):
         bound = 2.0 ** -8 * (absum + ref.abs()) * 1.01 + 1e-5
         err = (got - ref).abs()
         assert bool((err <= bound).all()), float((err - bound).max())
+    # head 0 of the reassembled result against the oracle of the global problem
+    scale = np.float32(1.0 / np.sqrt(d))
+    q64, k64, v64, do64 = (f64(x[0, 0]) for x in (q, k, v, do))
+    O, LSE, dQ, dK, dV = whole_head_reference(q64, k64, v64, do64, global_vectors, np.arange(N),
+                                              scale)
+    tol = TOL["bf16"]
+    assert_close("cp16 O", f64(o_re), O, tol)
+    assert_lse(f64(lse_re), LSE)
+    assert_close("cp16 dQ", f64(dq_re), dQ, tol)
+    assert_close("cp16 dK (sum over ranks)", f64(dk_sum[0, 0]), dK, tol)
+    assert_close("cp16 dV (sum over ranks)", f64(dv_sum[0, 0]), dV, tol)

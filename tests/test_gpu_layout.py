@@ -9,8 +9,10 @@ grouped key/value heads and per-batch / per-head mask vectors.
   float32 and rounded to bf16 once; against the bf16 per-head results of the repeated run the
   difference is at most 2^-8 (sum of |parts| + |result|) plus float32 reordering.
 * Against the float64 oracle, applied per (batch, head) with that head's key/value head and mask
-  set: O, dQ within 2e-2, LSE within 1e-3; a grouped dK / dV is a sum of G oracle gradients, each
-  within 2e-2 of the kernel's share, so the bound is G * 2e-2.
+  set: O, dQ within 2e-2, LSE within 1e-3; a grouped dK / dV against the sum of its G heads'
+  oracle gradients within the same 2e-2 (the kernel sums the G heads in float32 and rounds
+  once).  dO is scaled by 1 / sqrt(G) so that the grouped sums (about sqrt(G) times one head's
+  gradient) stay below 8, where bf16 storage resolves 2e-2.
 """
 
 import math
@@ -20,7 +22,7 @@ import pytest
 import torch
 
 import oracle
-from tests.parity import TOL, TOL_LSE, dev_i32, f64
+from tests.parity import TOL, TOL_LSE, assert_close, dev_i32, f64
 from workloads import masks
 
 pytestmark = pytest.mark.gpu
@@ -101,6 +103,7 @@ def test_grouped_heads(fm, H, H_kv, kind):
     g = torch.Generator().manual_seed(12 + H)
     q, do = randn(g, B, H, n, d), randn(g, B, H, n, d)
     k, v = randn(g, B, H_kv, n, d), randn(g, B, H_kv, n, d)
+    do = (do.float() / math.sqrt(G)).to(torch.bfloat16)
     scale = float(np.float32(1.0 / math.sqrt(d)))
     print(f"grouped heads H={H} H_kv={H_kv} mask={kind}", flush=True)
     o_x, lse_x = fm.fwd_ex(q, k, v, *vec, scale)
@@ -130,8 +133,8 @@ def test_grouped_heads(fm, H, H_kv, kind):
         assert np.abs(f64(dq_x[:, h:h + 1]) - dQ).max() <= TOL["bf16"], h
         dK[:, hk:hk + 1] += dKh
         dV[:, hk:hk + 1] += dVh
-    assert np.abs(f64(dk_x) - dK).max() <= G * TOL["bf16"]
-    assert np.abs(f64(dv_x) - dV).max() <= G * TOL["bf16"]
+    assert_close(f"grouped dK G={G}", f64(dk_x), dK, TOL["bf16"])
+    assert_close(f"grouped dV G={G}", f64(dv_x), dV, TOL["bf16"])
 
 
 @pytest.mark.parametrize("mask_b,mask_h,H_kv", [(1, 4, 4), (2, 1, 4), (2, 4, 4), (2, 4, 2)])

@@ -95,12 +95,21 @@ def test_classify_workloads_at_kernel_tiles(fm, key):
         compare_classify(got, oracle.classify(*v, w.nq, BM, BN), BM, BN)
 
 
-def test_classify_128k_swa_forward_tiles(fm):
-    w = configs.WORKLOADS["c4swa"]
+@pytest.mark.parametrize("key", ["c4swa", "c4doc"])
+def test_classify_128k_at_both_kernel_grids(fm, key):
+    """The 128K masks at the tile grids the attention calls really walk there: the forward and
+    dQ kernels' row lists at BM_fwd x BN_fwd, and the dK/dV kernel's column lists at BM_bwd x
+    2*BN_bwd (for nq >= 65536 its key blocks are twice as wide)."""
+    w = configs.WORKLOADS[key]
     v = configs.global_mask(w)
-    got = fm.classify(*[dev_i32(x) for x in v], w.nq, 128, 64, qlists=True, klists=True)
-    torch.cuda.synchronize()
-    compare_classify(got, oracle.classify(*v, w.nq, 128, 64), 128, 64)
+    bm_f, bn_f, bm_b, bn_b = fm.tile_sizes(torch.bfloat16, w.d)
+    assert w.nq >= 65536
+    dv = [dev_i32(x) for x in v]
+    for BM, BN in ((bm_f, bn_f), (bm_b, 2 * bn_b)):
+        print(f"classify {key} BM={BM} BN={BN}", flush=True)
+        got = fm.classify(*dv, w.nq, BM, BN, qlists=True, klists=True)
+        torch.cuda.synchronize()
+        compare_classify(got, oracle.classify(*v, w.nq, BM, BN), BM, BN)
 
 
 @pytest.mark.parametrize("seed", range(16))

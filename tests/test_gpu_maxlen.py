@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle
-from tests.parity import TOL, TOL_LSE, f64
+from tests.parity import (TOL, TOL_LSE, assert_close, assert_lse, cols_reference, f64,
+                          rows_reference)
 from workloads import masks
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -106,3 +107,81 @@ def test_long_query_short_walks(fm, dt, w):
                                     rows_of(do, r0, r1), M, scale, cols=np.array([j - k0]))
         assert np.abs(rows_of(dk, j, j + 1) - dK).max() <= tol, j
         assert np.abs(rows_of(dv, j, j + 1) - dV).max() <= tol, j
+
+
+def test_long_query_grouped_heads_with_per_head_masks(fm):
+    """The grouped-head (G > 1) instantiation of the dK/dV kernel's 8-wave shape (nq >= 65536,
+    three tile buffers), which walks the tile lists of a group's query heads as one sequence and
+    points rows past nq at the buffer end: H = 4 query heads over H_kv = 2 key/value heads, one
+    mask set per head, and in the first group a head whose every list is empty (every key fully
+    masked), so the walk moves from a head with tiles across one without any.  nq = nk =
+    65536 + 77 leaves ragged last blocks.  Sampled rows (O, LSE, dQ) per query head and sampled
+    key columns (dK, dV summed over the group's heads) against the oracle on exact
+    sub-problems; every output against per-head plain calls on the same data."""
+    n, d, H, H_kv = 65536 + 77, 128, 4, 2
+    G = H // H_kv
+    r = np.random.default_rng(np.random.SeedSequence([65613, 4]))
+    full = (np.zeros(n, np.int32), np.full(n, n, np.int32), np.zeros(n, np.int32),
+            np.zeros(n, np.int32))
+    sets = [masks.sliding_window(n, 300), full, masks.sliding_window(n, 2000),
+            masks.document(n, masks.uniform_cut_lengths(r, n, 48))]
+    vec = [torch.from_numpy(np.ascontiguousarray(np.stack([s_[i] for s_ in sets]))).cuda()
+           for i in range(4)]                                          # [H, nk] each
+    g = torch.Generator(device="cuda").manual_seed(4242)
+    q, do = (torch.randn((1, H, n, d), generator=g, device="cuda").to(torch.bfloat16)
+             for _ in range(2))
+    k, v = (torch.randn((1, H_kv, n, d), generator=g, device="cuda").to(torch.bfloat16)
+            for _ in range(2))
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    print("long query, grouped heads H=4 H_kv=2, per-head masks (one head fully masked)",
+          flush=True)
+    o, lse = fm.fwd_ex(q, k, v, *vec, scale)
+    dq, dk, dv = fm.bwd_ex(q, k, v, o, do, lse, *vec, scale)
+    torch.cuda.synchronize()
+    # per-head plain calls: O, LSE, dQ bit for bit; grouped dK, dV within the bf16 bound of
+    # the per-head sums
+    dk_sum = torch.zeros(1, H_kv, n, d, device="cuda")
+    dv_sum, dk_abs, dv_abs = (torch.zeros_like(dk_sum) for _ in range(3))
+    for h in range(H):
+        hk = h // G
+        sv = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in sets[h]]
+        qs, dos = q[:, h:h + 1].contiguous(), do[:, h:h + 1].contiguous()
+        ks, vs = k[:, hk:hk + 1].contiguous(), v[:, hk:hk + 1].contiguous()
+        o1, lse1 = fm.fwd(qs, ks, vs, *sv, scale)
+        dq1, dk1, dv1 = fm.bwd(qs, ks, vs, o1, dos, lse1, *sv, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o[:, h:h + 1], o1) and torch.equal(lse[:, h:h + 1], lse1), h
+        assert torch.equal(dq[:, h:h + 1], dq1), h
+        dk_sum[:, hk] += dk1[:, 0].float()
+        dv_sum[:, hk] += dv1[:, 0].float()
+        dk_abs[:, hk] += dk1[:, 0].float().abs()
+        dv_abs[:, hk] += dv1[:, 0].float().abs()
+    assert not dq[:, 1].any() and bool(torch.isneginf(lse[:, 1]).all())
+    for got, ref, absum in ((dk, dk_sum, dk_abs), (dv, dv_sum, dv_abs)):
+        err = (got.float() - ref).abs()
+        assert bool((err <= 2.0 ** -8 * (absum + ref.abs()) * 1.01 + 1e-5).all())
+    # the oracle on exact sub-problems
+    tol = TOL["bf16"]
+    q64 = [f64(q[0, h]) for h in range(H)]
+    do64 = [f64(do[0, h]) for h in range(H)]
+    k64 = [f64(k[0, hk]) for hk in range(H_kv)]
+    v64 = [f64(v[0, hk]) for hk in range(H_kv)]
+    rows = np.array([0, 1, 299, 300, 4097, n // 2 + 3, n - 78, n - 1])
+    for h in range(H):
+        hk = h // G
+        O, LSE, dQ = rows_reference(q64[h], k64[hk], v64[hk], do64[h], sets[h], rows, rows,
+                                    scale)
+        assert_close(f"O h={h}", f64(o[0, h, rows]), O, tol)
+        assert_lse(f64(lse[0, h, rows]), LSE)
+        assert_close(f"dQ h={h}", f64(dq[0, h, rows]), dQ, tol)
+    cols = np.array([0, 127, 128, 4095, n // 2, n - 78, n - 1])
+    for hk in range(H_kv):
+        dK = np.zeros((len(cols), d))
+        dV = np.zeros((len(cols), d))
+        for h in range(hk * G, (hk + 1) * G):
+            a, b = cols_reference(q64[h], k64[hk], v64[hk], do64[h], sets[h], cols,
+                                  np.arange(n), scale)
+            dK += a
+            dV += b
+        assert_close(f"dK group {hk}", f64(dk[0, hk, cols]), dK, tol)
+        assert_close(f"dV group {hk}", f64(dv[0, hk, cols]), dV, tol)

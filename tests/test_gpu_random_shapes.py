@@ -3,7 +3,7 @@ float64 oracle: random batch and head counts, grouped key/value heads (G = 1..3)
 1..419 (square shapes also draw the structured mask families), both built dtypes.  Each case is
 its own test so a failure names its seed.  Bars as elsewhere: O, dQ within 2e-2 (bf16) or 1e-4
 (fp32), LSE within 1e-3 with identical -inf rows, and a grouped dK / dV (a sum of G per-head
-gradients) within G times the bar.  FM_RANDOM_CASES sets the number of cases (default 24); the
+gradients, formed in float32 and rounded once) within the same bar.  FM_RANDOM_CASES sets the number of cases (default 24); the
 first cases of a longer sweep are the default ones."""
 
 import math
@@ -84,7 +84,7 @@ def test_random_shape(fm, case):
     fin = np.isfinite(LSE)
     if fin.any():
         assert np.abs(got_lse[fin] - LSE[fin]).max() <= TOL_LSE
-    for name, got, want, bar in (("O", o, O, tol), ("dQ", dq, dQ, tol), ("dK", dk, dK, G * tol),
-                                 ("dV", dvv, dV, G * tol)):
+    for name, got, want, bar in (("O", o, O, tol), ("dQ", dq, dQ, tol), ("dK", dk, dK, tol),
+                                 ("dV", dvv, dV, tol)):
         err = np.abs(f64(got) - want).max()
         assert err <= bar, f"{name}: max-abs error {err:.3e} > {bar:.1e}"
