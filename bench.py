@@ -188,6 +188,124 @@ def cp_emulation(args):
     }), flush=True)
 
 
+MASK_SWEEP_EXPONENTS = tuple(range(20, 27))  # n = 2^20 .. 2^26 keys
+MASK_SWEEP_REPS = 20
+
+
+def mask_kernel_sweep(args):
+    """HBM throughput of the integer kernels on their own, timed with HIP events on the launch
+    stream: block min/max (K1: 16 B read per key, 32 B written per key block of 64) and
+    clip-shift-max localisation (K7: 16 B read + 16 B written per key; the CP share's two
+    chunks of 4096 rows) at n = 2^20 .. 2^26, and tile classification with list compaction (K2)
+    at the 128K tile grids.  Every call goes through the C ABI; the launch order is fixed and
+    printed in `plan`, so a rocprofv3 kernel trace of this run can be matched dispatch by
+    dispatch (``rocprof_summary sweep``)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import mask_aware_flashattention_amd as fm
+    from mask_aware_flashattention_amd import _lib
+    from workloads import configs, masks
+
+    lib = fm.load_library()
+    dev = torch.device("cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+    reps = args.steps if args.steps != 20 else MASK_SWEEP_REPS
+    plan, results = [], []
+
+    def timed(fn, n_calls):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_calls):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n_calls
+
+    for e in MASK_SWEEP_EXPONENTS:
+        n = 1 << e
+        # sliding-window vectors at this length (any values do: the kernels are data-oblivious
+        # except for the list lengths, which K1 and K7 do not produce)
+        vec = [torch.from_numpy(x).to(dev) for x in masks.sliding_window(n, 4096)]
+        out = [torch.empty_like(x) for x in vec]
+        BN = 64
+        n_kb = -(-n // BN)
+        ws = torch.empty(lib.flashmask_classify_workspace_bytes(n, BN), dtype=torch.uint8,
+                         device=dev)
+
+        def k1():
+            # all outputs NULL: only the block min/max kernel runs (one query block, so the
+            # tile-count limit does not apply)
+            st = lib.flashmask_classify(*[P(x) for x in vec], n, n, n, BN, P(None), P(None),
+                                        P(None), P(None), P(None), P(ws), ws.numel(), stream)
+            assert st == 0, st
+        starts = (ctypes.c_int32 * 2)(*[c * n // 32 for c in configs.C5_CHUNKS])
+        lens = (ctypes.c_int32 * 2)(n // 32, n // 32)
+        n_local = ctypes.c_int32()
+
+        def k7():
+            st = lib.flashmask_localize(*[P(x) for x in vec], n, n, starts, lens, 2,
+                                        *[P(x) for x in out], ctypes.byref(n_local), stream)
+            assert st == 0, st
+        for name, fn, nbytes in (("block_minmax_kernel", k1, 16 * n + 32 * n_kb),
+                                 ("localize_kernel", k7, 32 * n)):
+            plan.append({"kernel": name, "n": n, "calls": 2 + reps})
+            t = timed(fn, reps)
+            results.append({"kernel": name, "n": n, "bytes": nbytes, "us": round(t * 1e6, 3),
+                            "GB/s": round(nbytes / t / 1e9, 1),
+                            "frac_of_hbm_peak": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)})
+        del vec, out, ws
+
+    # K2 at the 128K grids: row lists at the forward tiles (128 x 64) and column lists at the
+    # 8-wave backward tiles (64 x 128), both 128K masks.
+    for key in ("c4swa", "c4doc"):
+        w = configs.WORKLOADS[key]
+        vec = [torch.from_numpy(x).to(dev) for x in configs.global_mask(w)]
+        for BM, BN, rows in ((128, 64, True), (64, 128, False)):
+            n_qb, n_kb = -(-w.nq // BM), -(-w.nk // BN)
+            ws = torch.empty(lib.flashmask_classify_workspace_bytes(w.nk, BN), dtype=torch.uint8,
+                             device=dev)
+            cnt = torch.empty(n_qb if rows else n_kb, dtype=torch.int32, device=dev)
+            lst = torch.empty(n_qb * n_kb, dtype=torch.int32, device=dev)
+            args_q = (P(cnt), P(lst), P(None), P(None)) if rows else (P(None), P(None), P(cnt),
+                                                                       P(lst))
+
+            def k12():
+                st = lib.flashmask_classify(*[P(x) for x in vec], w.nq, w.nk, BM, BN, P(None),
+                                            *args_q, P(ws), ws.numel(), stream)
+                assert st == 0, st
+
+            def k1only():
+                st = lib.flashmask_classify(*[P(x) for x in vec], w.nq, w.nk, BM, BN, P(None),
+                                            P(None), P(None), P(None), P(None), P(ws), ws.numel(),
+                                            stream)
+                assert st == 0, st
+            plan.append({"kernel": "block_minmax_kernel+classify_kernel", "workload": key,
+                         "BM": BM, "BN": BN, "orientation": "rows" if rows else "columns",
+                         "calls": 2 + reps})
+            t12 = timed(k12, reps)
+            plan.append({"kernel": "block_minmax_kernel", "workload": key, "BM": BM, "BN": BN,
+                         "calls": 2 + reps})
+            t1 = timed(k1only, reps)
+            listed = int(cnt.sum())
+            nbytes = 32 * n_kb + 4 * (listed + cnt.numel())  # table once, lists and counts
+            t2 = max(t12 - t1, 1e-9)
+            results.append({"kernel": "classify_kernel", "workload": key, "BM": BM, "BN": BN,
+                            "orientation": "rows" if rows else "columns",
+                            "tiles": n_qb * n_kb, "listed": listed, "bytes": nbytes,
+                            "us": round(t2 * 1e6, 3), "GB/s": round(nbytes / t2 / 1e9, 1),
+                            "Gtiles/s": round(n_qb * n_kb / t2 / 1e9, 2)})
+    print(json.dumps({"metric": "integer kernels: HBM GB/s (algorithmic bytes / event time)",
+                      "unit": "GB/s", "peak_GB/s": PEAK_HBM_GBS, "reps": reps,
+                      "results": results, "plan": plan}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,6 +335,9 @@ def main():
         sys.exit(1)
     if args.workload == "cp16":
         cp_emulation(args)
+        return
+    if args.workload == "masksweep":
+        mask_kernel_sweep(args)
         return
     lib = fm.load_library()
     dev = torch.device("cuda:0")

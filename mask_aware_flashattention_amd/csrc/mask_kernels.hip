@@ -74,6 +74,63 @@ __global__ __launch_bounds__(256) void block_minmax_kernel(MaskVecs v, int64_t v
   }
 }
 
+// The same per key block min/max for blocks of BN = 4 * LPB keys (64 or 128, the attention
+// kernels' key-block widths) with 16-byte aligned vectors: LPB lanes share a block, each loading
+// four consecutive keys of every vector with one 16-byte load (whole 64-byte segments per group
+// of four lanes), and the 8 results are reduced over those lanes.  A wave covers 64 / LPB blocks;
+// keys past nk are read one by one, never as part of a 16-byte load.
+template <int LPB>
+__global__ __launch_bounds__(256) void block_minmax_vec_kernel(MaskVecs v, int64_t vec_stride,
+                                                               int32_t nk, int32_t n_kb,
+                                                               int32_t* __restrict__ mm) {
+  constexpr int BN = 4 * LPB, BPW = kWave / LPB;
+  const int64_t set = blockIdx.y;
+  const int32_t* src[4] = {v.lts + set * vec_stride, v.lte + set * vec_stride,
+                           v.uts + set * vec_stride, v.ute + set * vec_stride};
+  mm += set * 8 * n_kb;
+  const int lane = lane_id();
+  const int li = lane % LPB;
+  const int64_t kb = ((int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)) * BPW + lane / LPB;
+  int32_t lo[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+  int32_t hi[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
+  if (kb < n_kb) {
+    const int64_t j = kb * BN + 4 * li;
+    if (j + 3 < nk) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int4 x = *reinterpret_cast<const int4*>(src[t] + j);
+        const int32_t a = x.x < x.y ? x.x : x.y, b = x.z < x.w ? x.z : x.w;
+        const int32_t c = x.x > x.y ? x.x : x.y, d = x.z > x.w ? x.z : x.w;
+        lo[t] = a < b ? a : b;
+        hi[t] = c > d ? c : d;
+      }
+    } else {
+      for (int64_t e = j; e < nk && e < j + 4; ++e)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int32_t x = src[t][e];
+          lo[t] = x < lo[t] ? x : lo[t];
+          hi[t] = x > hi[t] ? x : hi[t];
+        }
+    }
+  }
+#pragma unroll
+  for (int off = LPB / 2; off >= 1; off >>= 1)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int32_t a = __shfl_xor(lo[t], off), b = __shfl_xor(hi[t], off);
+      lo[t] = a < lo[t] ? a : lo[t];
+      hi[t] = b > hi[t] ? b : hi[t];
+    }
+  if (li == 0 && kb < n_kb) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      mm[(2 * t) * n_kb + kb] = lo[t];
+      mm[(2 * t + 1) * n_kb + kb] = hi[t];
+    }
+  }
+}
+
 struct BlockBounds {
   int32_t lts_lo, lts_hi, lte_lo, lte_hi, uts_lo, uts_hi, ute_lo, ute_hi;
 };
@@ -310,6 +367,18 @@ __global__ __launch_bounds__(kOrderThreads) void block_order_kernel(const int32_
 hipError_t launch_block_minmax(MaskVecs v, int32_t nk, int32_t BN, int32_t* mm,
                                hipStream_t stream, int32_t sets, int64_t vec_stride) {
   const int32_t n_kb = (nk + BN - 1) / BN;
+  const uintptr_t all = (uintptr_t)v.lts | (uintptr_t)v.lte | (uintptr_t)v.uts | (uintptr_t)v.ute;
+  if ((BN == 64 || BN == 128) && (all & 15) == 0 && (sets == 1 || vec_stride % 4 == 0)) {
+    const int bpw = kWave / (BN / 4);  // key blocks per wave
+    const int64_t grid = ((int64_t)n_kb + bpw * kWavesPerBlock - 1) / (bpw * kWavesPerBlock);
+    if (BN == 64)
+      hipLaunchKernelGGL(block_minmax_vec_kernel<16>, dim3((unsigned)grid, sets), dim3(256), 0,
+                         stream, v, vec_stride, nk, n_kb, mm);
+    else
+      hipLaunchKernelGGL(block_minmax_vec_kernel<32>, dim3((unsigned)grid, sets), dim3(256), 0,
+                         stream, v, vec_stride, nk, n_kb, mm);
+    return hipGetLastError();
+  }
   const int grid = (n_kb + kWavesPerBlock - 1) / kWavesPerBlock;
   hipLaunchKernelGGL(block_minmax_kernel, dim3(grid, sets), dim3(256), 0, stream, v, vec_stride, nk,
                      BN, n_kb, mm);

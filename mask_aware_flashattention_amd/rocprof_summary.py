@@ -12,6 +12,13 @@
       with --calibration-copy-mib N (known bytes / counter bytes).  Prints one JSON object that
       also records the hash of the kernel sources, so the benchmark can tell when the counters
       no longer describe the current kernel.
+
+  python -m mask_aware_flashattention_amd.rocprof_summary sweep KERNEL_TRACE_CSV SWEEP_JSON
+         [--command C]
+      per-size durations of the integer kernels from a kernel trace (``-f csv``) of
+      ``bench.py --workload masksweep``: the sweep prints its launch plan in a fixed order, and
+      the trace's dispatches of those kernels are matched to it in dispatch order (the first two
+      calls of each entry are warm-up); GB/s = the sweep's algorithmic bytes / average duration.
 """
 
 from __future__ import annotations
@@ -90,6 +97,74 @@ def cmd_traffic(a):
     print(json.dumps(rec, indent=1))
 
 
+SWEEP_KERNELS = ("block_minmax_kernel", "classify_kernel", "localize_kernel")
+
+
+def _trace_rows(csv_path):
+    import csv
+    with open(csv_path, newline="") as fh:
+        rows = list(csv.DictReader(fh))
+    out = []
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        # the block min/max has a vectorised variant for 64- and 128-key blocks
+        short = next((k for k in SWEEP_KERNELS if k in name or
+                      (k == "block_minmax_kernel" and "block_minmax" in name)), None)
+        if short is None:
+            continue
+        did = int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0)
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3  # ns -> us
+        out.append((did, short, dur))
+    out.sort()
+    return [(k, d) for _, k, d in out]
+
+
+def cmd_sweep(a):
+    rec = json.load(open(a.sweep))
+    disp = _trace_rows(a.trace)
+    pos = 0
+    measured = []
+    for entry in rec["plan"]:
+        kernels = entry["kernel"].split("+")
+        durs = {k: [] for k in kernels}
+        for call in range(entry["calls"]):
+            for k in kernels:
+                if pos >= len(disp) or disp[pos][0] != k:
+                    raise SystemExit(f"trace does not follow the plan at dispatch {pos}: "
+                                     f"expected {k}, found {disp[pos] if pos < len(disp) else None}")
+                if call >= 2:
+                    durs[k].append(disp[pos][1])
+                pos += 1
+        measured.append({k: sum(v) / len(v) for k, v in durs.items()})
+    print("# Integer kernels: rocprofv3 kernel-trace durations and HBM throughput\n")
+    if a.command:
+        print(f"Command:\n\n```\n{a.command}\n```\n")
+    print("| kernel | size | algorithmic bytes | avg (us) | GB/s | of 8 TB/s | event-timed GB/s |")
+    print("|---|---|---:|---:|---:|---:|---:|")
+    res = list(rec["results"])
+    k2 = [r for r in res if r["kernel"] == "classify_kernel"]
+    k17 = [r for r in res if r["kernel"] != "classify_kernel"]
+    i17 = 0
+    i2 = 0
+    for entry, m in zip(rec["plan"], measured):
+        if "workload" not in entry:
+            r = k17[i17]
+            i17 += 1
+            us = m[r["kernel"]]
+            size = f"n = 2^{r['n'].bit_length() - 1}"
+        elif "classify_kernel" in m:
+            r = k2[i2]
+            i2 += 1
+            us = m["classify_kernel"]
+            size = (f"{r['workload']} {r['BM']}x{r['BN']} {r['orientation']}: {r['tiles']} tiles, "
+                    f"{r['listed']} listed")
+        else:
+            continue
+        gbs = r["bytes"] / (us * 1e-6) / 1e9
+        print(f"| `{r['kernel']}` | {size} | {r['bytes']} | {us:.2f} | {gbs:.1f} | "
+              f"{gbs / 8000.0:.3f} | {r['GB/s']} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -104,8 +179,12 @@ def main():
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--sources", default="bwd", choices=["bwd", "fwd"])
     t.add_argument("--command", default="")
+    w = sub.add_parser("sweep")
+    w.add_argument("trace")
+    w.add_argument("sweep")
+    w.add_argument("--command", default="")
     a = ap.parse_args()
-    {"kernels": cmd_kernels, "traffic": cmd_traffic}[a.cmd](a)
+    {"kernels": cmd_kernels, "traffic": cmd_traffic, "sweep": cmd_sweep}[a.cmd](a)
 
 
 if __name__ == "__main__":
