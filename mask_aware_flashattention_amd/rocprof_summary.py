@@ -19,6 +19,15 @@
       ``bench.py --workload masksweep``: the sweep prints its launch plan in a fixed order, and
       the trace's dispatches of those kernels are matched to it in dispatch order (the first two
       calls of each entry are warm-up); GB/s = the sweep's algorithmic bytes / average duration.
+
+  python -m mask_aware_flashattention_amd.rocprof_summary counters --pmc DB [DB ...]
+         --trace DB [--cus 256] [--simds 4] [--ses 32] [--command C]
+      per attention kernel: the counters of several --pmc runs (means per dispatch) and the
+      kernel's average duration from a kernel trace, with the derived rates: the loaded clock
+      (SQ_CYCLES over the shader engines), the fraction of SIMD cycles the matrix core is busy
+      (SQ_VALU_MFMA_BUSY_CYCLES), the vector ALU busy and co-issue fractions, instructions per
+      MFMA and LDS bytes read per CU and clock.  The kernel-source hashes of the forward and the
+      backward are recorded with it.
 """
 
 from __future__ import annotations
@@ -95,6 +104,68 @@ def cmd_traffic(a):
         "command": a.command,
     }
     print(json.dumps(rec, indent=1))
+
+
+def cmd_counters(a):
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench  # noqa: E402  (kernel-source hashes)
+
+    vals = {}
+    for db in a.pmc:
+        con = sqlite3.connect(db)
+        acc = {}
+        for k, c, v in con.execute("select kernel_name, counter_name, value from counters_collection"):
+            acc.setdefault((k, c), []).append(v)
+        con.close()
+        for (k, c), v in acc.items():
+            vals.setdefault(k, {})[c] = sum(v) / len(v)
+    durs = {name: avg for name, calls, total, avg, pct in kernel_stats(a.trace)}
+    simds = a.cus * a.simds
+    print("# Attention kernels: hardware counters at n = 32768 (40 log-normal documents)\n")
+    if a.command:
+        print(f"Commands:\n\n```\n{a.command}\n```\n")
+    print(f"Kernel sources: forward hash `{bench.kernel_source_hash('fwd')}`, backward hash "
+          f"`{bench.kernel_source_hash('bwd')}` (code without comments, as the benchmark checks).\n")
+    rows = []
+    for k, v in sorted(vals.items()):
+        if "attn_" not in k:
+            continue
+        dur = next((d for n, d in durs.items() if n == k), None)
+        if dur is None or "SQ_INSTS_MFMA" not in v:
+            continue
+        cyc = v["SQ_CYCLES"] / a.ses                   # clocks of one shader engine
+        clock = cyc / dur * 1e-3                       # GHz (duration in us)
+        simd_cycles = simds * cyc
+        mfma = v["SQ_INSTS_MFMA"]
+        busy = v["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles
+        valu = 4 * v["SQ_ACTIVE_INST_VALU"] / simd_cycles
+        coex = v["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cycles
+        rows.append((k, dur, clock, busy, valu, coex, 1 - (busy + valu - coex),
+                     v["SQ_INSTS_VALU"] / mfma, v["SQ_INSTS_VALU_TRANS_F32"] / mfma,
+                     v["SQ_INSTS_LDS"] / mfma,
+                     64 * v["SQ_INSTS_LDS_LOAD_BANDWIDTH"] / (a.cus * cyc),
+                     v["SQ_LDS_BANK_CONFLICT"], v.get("SQ_LDS_DATA_FIFO_FULL", 0),
+                     mfma * 32768 / (dur * 1e-6) / 1e12))
+    print("| kernel | avg (us) | clock (GHz) | MFMA busy | VALU busy | co-issue | neither | "
+          "VALU / MFMA | exp / MFMA | LDS instr / MFMA | LDS B/clk/CU | bank conflicts | "
+          "LDS data FIFO full | executed MFMA TFLOP/s |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for r in rows:
+        print(f"| `{r[0][:60]}` | {r[1]:.1f} | {r[2]:.2f} | {r[3]:.3f} | {r[4]:.3f} | {r[5]:.3f} | "
+              f"{r[6]:.3f} | {r[7]:.2f} | {r[8]:.2f} | {r[9]:.2f} | {r[10]:.1f} | {r[11]:.0f} | "
+              f"{r[12]:.3g} | {r[13]:.0f} |")
+    print("\nFractions are of SIMD cycles at the loaded clock (MFMA busy counts 32 cycles per "
+          "32x32x16 bf16 MFMA; VALU busy from SQ_ACTIVE_INST_VALU; co-issue = cycles with both; "
+          "neither = 1 - MFMA - VALU + co-issue).  Executed MFMA TFLOP/s counts every MFMA the "
+          "kernel issues (32768 FLOP each), masked entries of listed tiles and the backward's "
+          "recomputed products included; it is not the benchmark's useful-FLOP rate.")
+    print("\nRaw means per dispatch:\n")
+    names = sorted({c for k, v in vals.items() if "attn_" in k for c in v})
+    print("| counter | " + " | ".join(f"`{r[0][:40]}`" for r in rows) + " |")
+    print("|---|" + "---:|" * len(rows))
+    for c in names:
+        print(f"| {c} | " + " | ".join(f"{vals[r[0]].get(c, float('nan')):.4g}" for r in rows) + " |")
 
 
 SWEEP_KERNELS = ("block_minmax_kernel", "classify_kernel", "localize_kernel")
@@ -179,12 +250,20 @@ def main():
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--sources", default="bwd", choices=["bwd", "fwd"])
     t.add_argument("--command", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("--pmc", nargs="+", required=True)
+    c.add_argument("--trace", required=True)
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--simds", type=int, default=4)
+    c.add_argument("--ses", type=int, default=32)
+    c.add_argument("--command", default="")
     w = sub.add_parser("sweep")
     w.add_argument("trace")
     w.add_argument("sweep")
     w.add_argument("--command", default="")
     a = ap.parse_args()
-    {"kernels": cmd_kernels, "traffic": cmd_traffic, "sweep": cmd_sweep}[a.cmd](a)
+    {"kernels": cmd_kernels, "traffic": cmd_traffic, "sweep": cmd_sweep,
+     "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
