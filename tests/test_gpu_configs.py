@@ -21,7 +21,7 @@ from workloads import configs
 
 pytestmark = pytest.mark.gpu
 
-KEYS = ["c1", "c2a", "c2b", "c2c", "c2d", "c2e", "c2f", "c3", "c4swa", "c4doc", "c5"]
+KEYS = ["c1", "c2a", "c2b", "c2c", "c2d", "c2e", "c2f", "c3", "c3m", "c4swa", "c4doc", "c5"]
 
 
 @pytest.fixture(scope="module")

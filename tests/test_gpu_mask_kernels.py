@@ -79,7 +79,7 @@ def compare_classify(got, want, BM, BN):
         assert np.array_equal(klist[kb, :len(lst)], lst), kb
 
 
-@pytest.mark.parametrize("key", ["c1", "c2a", "c2b", "c2c", "c2d", "c2e", "c2f", "c3", "c5"])
+@pytest.mark.parametrize("key", ["c1", "c2a", "c2b", "c2c", "c2d", "c2e", "c2f", "c3", "c3m", "c5"])
 def test_classify_workloads_at_kernel_tiles(fm, key):
     w = configs.WORKLOADS[key]
     v = configs.global_mask(w)

@@ -21,7 +21,7 @@ from workloads import configs
 pytestmark = pytest.mark.gpu
 
 # workload -> heads compared whole
-HEADS = {"c3": (0, 31), "c4swa": (0,), "c4doc": (0,), "c5": (0, 15)}
+HEADS = {"c3": (0, 31), "c3m": (0,), "c4swa": (0,), "c4doc": (0,), "c5": (0, 15)}
 
 
 @pytest.fixture(scope="module")

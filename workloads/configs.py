@@ -71,6 +71,11 @@ WORKLOADS = {
                     "block_sparse"),
     "c3": Workload("c3", 3, 0, "n32768 log-normal causal-document x40", "bf16", 1, 32, 32768,
                    32768, 128, 1.0, "document_lognormal", {"docs": 40}),
+    # The same generator at the draw whose unmasked count is the median of draws 0..199 (29.6M
+    # per head against 45.6M for draw 0, whose one 7,265-row document holds 58% of the work): a
+    # sensitivity case for the benchmark; Q/K/V/dO are those of the 32K workload.
+    "c3m": Workload("c3m", 3, 198, "n32768 log-normal causal-document x40, median-U draw",
+                    "bf16", 1, 32, 32768, 32768, 128, 1.0, "document_lognormal", {"docs": 40}),
     "c4swa": Workload("c4swa", 4, 0, "n131072 sliding-window w4096", "bf16", 1, 8, 131072,
                       131072, 128, 0.5, "sliding_window", {"w": 4096}),
     "c4doc": Workload("c4doc", 4, 1, "n131072 causal-document x16", "bf16", 1, 8, 131072,
