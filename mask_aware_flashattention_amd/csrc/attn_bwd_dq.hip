@@ -277,15 +277,19 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
     for (int rb = 0; rb < C::NRB; ++rb) {
       sacc[rb] = f32x16{};
       pacc[rb] = f32x16{};
+    }
+    // four independent accumulators in turn; the K / V reads run six products ahead
 #pragma unroll
-      for (int st = 0; st < C::QK_STEPS; ++st) {
+    for (int st = 0; st < C::QK_STEPS; ++st)
+#pragma unroll
+      for (int rb = 0; rb < C::NRB; ++rb) {
         const int off = off_s[st] + rb * 32 * C::ROW_BYTES;
         const frag ka = *reinterpret_cast<const frag*>(kt + off);
         const frag va = *reinterpret_cast<const frag*>(vt + off);
         sacc[rb] = E::mfma(ka, qf[st], sacc[rb]);
         pacc[rb] = E::mfma(va, dof[st], pacc[rb]);
       }
-    }
+    if constexpr (KPL == 8) sched_mfma_reads_ahead<2 * C::NRB * C::QK_STEPS, 1, 6>();
 
     if (test) {
       const uint32_t* mw = mwp(bufc) + w * C::BN;
@@ -321,6 +325,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
         dq_acc[db] = E::mfma(tr_operand(kt, off_tk[db], t * KSTEP * C::ROW_BYTES), sf[t], dq_acc[db]);
+    if constexpr (KPL == 8) sched_mfma_reads_ahead<C::KV_STEPS * C::NDB, 2, 3>();  // K^T 3 ahead
 
     if (next_test) mask_store(mk, other);
     entry = next;

@@ -236,20 +236,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     const unsigned char* vt = kt + C::TILE_BYTES;
 
     // S^T = K Q^T: register r of group g in row block rb is tile key rb*32 + perm_index(r, g);
-    // the column is this lane's query.
+    // the column is this lane's query.  The two row blocks' products alternate (independent
+    // accumulators), and the K reads run six products ahead of their use.
     f32x16 sacc[C::NRB];
 #pragma unroll
-    for (int rb = 0; rb < C::NRB; ++rb) {
-      sacc[rb] = f32x16{};
+    for (int rb = 0; rb < C::NRB; ++rb) sacc[rb] = f32x16{};
 #pragma unroll
-      for (int st = 0; st < C::QK_STEPS; ++st) {
+    for (int st = 0; st < C::QK_STEPS; ++st)
+#pragma unroll
+      for (int rb = 0; rb < C::NRB; ++rb) {
         sacc[rb] = E::mfma(*reinterpret_cast<const frag*>(kt + off_k[st] + rb * 32 * C::ROW_BYTES),
                            qf[st], sacc[rb]);
         constexpr int every = C::QK_STEPS * C::NRB / 4;
-        if ((rb * C::QK_STEPS + st) % every == every - 1)
-          stage_part(next, other, (rb * C::QK_STEPS + st) / every);
+        if ((st * C::NRB + rb) % every == every - 1) stage_part(next, other, (st * C::NRB + rb) / every);
       }
-    }
+    if constexpr (KPL == 8) sched_mfma_reads_ahead<C::QK_STEPS * C::NRB, 1, 6>();
 
     if (test) {
       const uint32_t* mw = mwp(bufc) + w * C::BN;
@@ -320,6 +321,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
         oacc[db] = E::mfma(vf, pf[t], oacc[db]);
       }
     }
+    if constexpr (KPL == 8) sched_mfma_reads_ahead<C::PV_STEPS * C::NDB, 2, 3>();  // V^T 3 ahead
     if (next_test) mask_store(mk, other);
     entry = next;
   };

@@ -249,4 +249,24 @@ __device__ inline s16x4 lds_read_tr16(const void* p) {
       (lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
 }
 
+// ---- scheduling hint for a run of MFMAs fed from LDS -----------------------------------------
+// Placed right after a block of N MFMAs whose A operands are LDS reads (R read instructions per
+// MFMA), it asks the compiler's scheduler to issue the reads of the first AHEAD MFMAs up front and
+// then alternate one MFMA with the reads of the MFMA AHEAD places later, so each MFMA finds its
+// operand about AHEAD MFMAs after requesting it.  (Without it the compiler keeps one or two reads
+// in flight where registers are scarce and waits for each operand just before its MFMA.)  Only
+// the order of instructions changes: the waits the compiler inserts stay exact.
+template <int N, int R, int AHEAD>
+__device__ inline void sched_mfma_reads_ahead() {
+  static_assert(AHEAD > 0 && AHEAD <= N, "lead within the run");
+  constexpr int kMfma = 0x008, kDsRead = 0x100;  // instruction classes of the scheduler hint
+  __builtin_amdgcn_sched_group_barrier(kDsRead, R * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
+}
+
 }  // namespace fm
