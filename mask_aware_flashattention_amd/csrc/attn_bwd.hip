@@ -14,7 +14,10 @@
 //                  the dS wave keeps V rows, computes dP = dO V^T, takes P from the P wave
 //                  through LDS, forms dS = P (dP - D) and accumulates dK^T += Q^T dS.
 //                Each wave then needs under 256 registers, so two run on every SIMD and one's
-//                elementwise work overlaps the other's matrix products.  The workgroup walks
+//                elementwise work overlaps the other's matrix products (in the 4-wave shape the
+//                two waves of a SIMD belong to the two workgroups on the CU and have the same
+//                role; in the 8-wave shape waves w and w + 4, the P and dS waves of key group w,
+//                share a SIMD).  The workgroup walks
 //                the query blocks (BM = 64 rows) of its list in 32-row units; Q and dO rows
 //                are A operands read from LDS in a permuted row order so the accumulators
 //                double as operands, Q^T and dO^T come from the gfx950 LDS transpose read.
@@ -376,8 +379,8 @@ __global__ __launch_bounds__(128 * NG, sizeof(T) == 2 ? 4 / NG : 1) void attn_bw
   };
 
   // One step per 32-query unit, one workgroup barrier per step (publish).  The dS wave runs one
-  // unit behind the P wave, so the two waves of a SIMD alternate between matrix and vector work
-  // instead of contending for the matrix core at the same time:
+  // unit behind the P wave, so that between two barriers both waves of a pair have their matrix
+  // products and their vector work to interleave (neither waits for the other's products):
   //   P wave,  unit (qt, h):  S = Q K^T; P = exp2(S*scale*log2e - LSE2), 0 where masked; P to
   //                           exchange slot h; barrier; dV^T += dO^T P.
   //   dS wave:                the pending unit (qp, 1-h), whose P was published at the previous
