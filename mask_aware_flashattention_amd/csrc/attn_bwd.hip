@@ -15,12 +15,13 @@
 //                  through LDS, forms dS = P (dP - D) and accumulates dK^T += Q^T dS.
 //                Each wave then needs under 256 registers, so two run on every SIMD and one's
 //                elementwise work overlaps the other's matrix products (in the 4-wave shape the
-//                two waves of a SIMD belong to the two workgroups on the CU and have the same
-//                role; in the 8-wave shape waves w and w + 4, the P and dS waves of key group w,
-//                share a SIMD).  The workgroup walks
-//                the query blocks (BM = 64 rows) of its list in 32-row units; Q and dO rows
-//                are A operands read from LDS in a permuted row order so the accumulators
-//                double as operands, Q^T and dO^T come from the gfx950 LDS transpose read.
+//                two waves of a SIMD belong to the two workgroups on the CU, and which SIMD gets
+//                which wave varies between workgroups, so their roles mix; in the 8-wave shape
+//                waves w and w + 4, the P and dS waves of key group w, share a SIMD).  The
+//                workgroup walks the query blocks (BM = 64 rows) of its list in 32-row units;
+//                Q and dO rows are A operands read from LDS in a permuted row order so the
+//                accumulators double as operands, Q^T and dO^T come from the gfx950 LDS
+//                transpose read.
 //                Q/dO tiles go from HBM straight into two LDS buffers (three in the 8-wave
 //                shape), each requested while the one before it (the two before it) compute;
 //                one workgroup barrier per unit (P handed over) also publishes the next tile,
