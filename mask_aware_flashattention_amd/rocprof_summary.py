@@ -106,6 +106,31 @@ def cmd_traffic(a):
     print(json.dumps(rec, indent=1))
 
 
+def cmd_workloads(a):
+    """Markdown table of `bench.py` JSON lines, one per workload (the benchmark's own HIP-event
+    timings; no profiler involved)."""
+    print("| workload | U per head | step ms | fwd+bwd TFLOP/s | fwd kernel TFLOP/s | fwd frac | "
+          "bwd kernels TFLOP/s | bwd frac | oracle TFLOP/s (cores) |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+    with open(a.jsonl) as fh:
+        for line in fh:
+            if not line.strip():
+                continue
+            d = json.loads(line)
+            c = d["config"]
+            u = c.get("unmasked_per_head")
+            if "roofline_fwd" in d:
+                cb = d.get("cpu_baseline") or {}
+                oracle = (f"{cb['value']:.4f} ({cb['cores']})" if "value" in cb else "—")
+                print(f"| {c['workload']} | {u:,} | {d['ms_per_step']:.3f} | {d['value']:.1f} | "
+                      f"{d['roofline_fwd']['achieved']:.1f} | {d['roofline_fwd']['frac']:.3f} | "
+                      f"{d['roofline']['achieved']:.1f} | {d['roofline']['frac']:.3f} | {oracle} |")
+            else:  # the all-ranks emulation: whole step only, and one global call beside it
+                print(f"| {c['workload']} | {u:,} | {d['ms_per_step']:.3f} | {d['value']:.1f} | — | — "
+                      f"| — | — | — (one global call: {d['global_call_ms']:.3f} ms, "
+                      f"{d['global_call_tflops']:.1f} TFLOP/s) |")
+
+
 def cmd_counters(a):
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     sys.path.insert(0, root)
@@ -257,13 +282,15 @@ def main():
     c.add_argument("--simds", type=int, default=4)
     c.add_argument("--ses", type=int, default=32)
     c.add_argument("--command", default="")
+    b = sub.add_parser("workloads")
+    b.add_argument("jsonl")
     w = sub.add_parser("sweep")
     w.add_argument("trace")
     w.add_argument("sweep")
     w.add_argument("--command", default="")
     a = ap.parse_args()
     {"kernels": cmd_kernels, "traffic": cmd_traffic, "sweep": cmd_sweep,
-     "counters": cmd_counters}[a.cmd](a)
+     "counters": cmd_counters, "workloads": cmd_workloads}[a.cmd](a)
 
 
 if __name__ == "__main__":
