@@ -3,9 +3,9 @@
 // O(tiles)) scans bound by HBM bandwidth or launch latency; none touches the matrix cores.
 //
 // Sources: "FlashMask-3 sends each GPU its mask without sending any mask" (learnaivisually.com),
-// tile-classification paragraph (min/max along the key axis, three tile classes, a queue of the
-// valid blocks) and clip-shift-max paragraph; "FlashMask-3: Efficient and Expressive Mask-Aware
-// Distributed Attention", abstract (zero-communication localisation).
+// tile-classification paragraph (per-key-block extremes of the vectors, three tile classes, a
+// queue of the valid blocks) and clip-shift-max paragraph; "FlashMask-3: Efficient and
+// Expressive Mask-Aware Distributed Attention", abstract (zero-communication localisation).
 #include <limits.h>
 
 #include "fm_common.hpp"
