@@ -250,9 +250,10 @@ __global__ __launch_bounds__(128 * NG, sizeof(T) == 2 ? 4 / NG : 1) void attn_bw
   Cursor first{0, 0, 0, nullptr};
   head_list(first);
   load_mask(first.gi);
-  // Wait for these loads here: the main loop keeps tile loads in flight, and a wait the compiler
-  // would place there for a register loaded now would also wait for those.
-  wait_vmem();
+  // The K/V rows and the mask values are waited for before the walk, together with the first
+  // tile's loads (issued below, so that the two requests overlap): the main loop keeps tile loads
+  // in flight, and a wait the compiler would place there for a register loaded now would also
+  // wait for those.
 
   // A tile's 64 rows of Q, then of dO, are 32 blocks of 1 KiB; wave w moves blocks
   // BPW*w .. BPW*w + BPW - 1 (the P waves Q, the dS waves dO), lane l the 16-byte slot l of a
@@ -459,7 +460,7 @@ __global__ __launch_bounds__(128 * NG, sizeof(T) == 2 ? 4 / NG : 1) void attn_bw
       Cursor second = first;
       if (total > 1) advance(second);
       load_tile(second.gi, entry_of(second), I1{});  // tile 1, or tile 0 again (never read)
-      wait_vmem_n<C::LPT>();                         // tile 0 has landed
+      wait_vmem_n<C::LPT>();  // the rows, the mask values and tile 0 have landed
     } else {
       wait_vmem();
     }

@@ -136,30 +136,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
       dof[s] = __builtin_bit_cast(frag, buf_load4(dobuf, off, 0));
     }
   }
-  // D of this row from its O and dO: lanes l and l ^ 32 hold the two halves of the row.
-  float ndlt;  // -D
-  {
-    const T* __restrict__ Op = static_cast<const T*>(a.o) + qbase;
-    const buf_rsrc obuf = make_buf(Op, (uint32_t)(a.nq - 1) * qrs + C::ROW_BYTES);
-    float part = 0.0f;
-#pragma unroll
-    for (int s = 0; s < C::QK_STEPS; ++s) {
-      const uint32_t off = (uint32_t)q_row * qrs + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
-      if constexpr (KPL == 8) {
-        const frag of = __builtin_bit_cast(frag, buf_load16(obuf, off, 0));
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) part = fmaf((float)dof[s][e], (float)of[e], part);
-      } else {
-        const float of = __builtin_bit_cast(float, buf_load4(obuf, off, 0));
-        part = fmaf(dof[s], of, part);
-      }
-    }
-    ndlt = -pair_sum32(part);
-    if (row_ok && g == 0) {
-      a.delta[row_idx] = ndlt;
-      a.lse2[row_idx] = lse2;
-    }
-  }
+  float ndlt = 0.0f;  // -D of this lane's row, formed once the first tile is on its way
 
   const int32_t* __restrict__ lst = a.qlist + ((size_t)set * n_qb + qb) * a.list_stride;
   const int last_kb = (a.nk - 1) / C::BN;
@@ -336,6 +313,31 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
     issue_tile(entry, first);
     if (is_test(entry)) mask_store(mask_load(entry), first);
   }
+  // D of this row from its O and dO (lanes l and l ^ 32 hold the two halves of the row), read
+  // after the first tile's loads are issued so that the two requests overlap.
+  {
+    const T* __restrict__ Op = static_cast<const T*>(a.o) + qbase;
+    const buf_rsrc obuf = make_buf(Op, (uint32_t)(a.nq - 1) * qrs + C::ROW_BYTES);
+    float part = 0.0f;
+#pragma unroll
+    for (int s = 0; s < C::QK_STEPS; ++s) {
+      const uint32_t off = (uint32_t)q_row * qrs + (uint32_t)(s * KSTEP + g * KPL) * sizeof(T);
+      if constexpr (KPL == 8) {
+        const frag of = __builtin_bit_cast(frag, buf_load16(obuf, off, 0));
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) part = fmaf((float)dof[s][e], (float)of[e], part);
+      } else {
+        const float of = __builtin_bit_cast(float, buf_load4(obuf, off, 0));
+        part = fmaf(dof[s], of, part);
+      }
+    }
+    ndlt = -pair_sum32(part);
+    if (row_ok && g == 0) {
+      a.delta[row_idx] = ndlt;
+      a.lse2[row_idx] = lse2;
+    }
+  }
+
   // Unrolled by two so each buffer index is a compile-time constant; an odd last tile runs after
   // the loop, so the loop body has no conditional path the accumulators must merge across.
   int it = 0;
