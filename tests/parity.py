@@ -65,8 +65,8 @@ def cols_reference(q, k, v, do, vectors, cols, mask_rows_all, scale):
 
 
 def oracle_workers():
-    """Worker threads for the whole-head oracle: the host's cores, at most 16 (a GPU machine's share
-    of its host)."""
+    """Worker threads for the whole-head oracle: the cores this process may use, at most 16 (the
+    host share one GPU typically gets)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
