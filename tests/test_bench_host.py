@@ -42,3 +42,18 @@ def test_source_hash_ignores_comments_only():
     other = "int f(int x) {\n  return x + 2;\n}\n"
     assert bench.code_text(src) == bench.code_text(same)
     assert bench.code_text(src) != bench.code_text(other)
+
+
+def test_workloads_table_renders_the_committed_lines():
+    """The per-workload table in the profiles is made from the committed bench lines."""
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    path = os.path.join(root, "profiles", "bench_workloads.jsonl")
+    r = subprocess.run([sys.executable, "-m", "mask_aware_flashattention_amd.rocprof_summary",
+                        "workloads", path], capture_output=True, text=True, cwd=root)
+    assert r.returncode == 0, r.stderr
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("| ") and "---" not in ln]
+    with open(path) as fh:
+        n = sum(1 for ln in fh if ln.strip())
+    assert len(lines) == n + 1  # header + one row per bench line
+    assert any("one global call" in ln for ln in lines)
