@@ -121,7 +121,32 @@ def cpu_baseline(w, vectors, tensors, mask_rows, seconds: float):
                    f"backward against all {w.nk} keys, {dt:.1f} s; throughput counts the "
                    f"sample's {u} unmasked entries at 14*d FLOPs each"),
         "seconds": dt,
+        "host": host_info(),
     }
+
+
+def host_info():
+    """The CPU model and the numpy / BLAS builds the CPU baseline ran on."""
+    import platform
+
+    import numpy as np
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                       if i.get("user_api") == "blas"})
+    except Exception:  # threadpoolctl missing or unable to inspect: leave the BLAS field empty
+        blas = []
+    return {"cpu_model": model, "numpy": np.__version__, "blas": blas}
 
 
 def cp_emulation(args):
