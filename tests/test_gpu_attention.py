@@ -129,3 +129,46 @@ def test_every_walk_length(fm, tiles):
     its two-buffer rotation over an even or odd number of tiles, and both column groups of a key
     block (nk = 160: two full 64-key blocks and a ragged one of 32 keys)."""
     run_case(fm, "bf16", 1, 1, 64 * tiles - 5, 160, "none", seed=tiles)
+
+
+@pytest.mark.parametrize("dtype,std,kind", [("bf16", 3.0, "document"), ("bf16", 6.0, "random"),
+                                            ("bf16", 6.0, "causal"), ("fp32", 2.0, "document")])
+def test_peaked_scores(fm, dtype, std, kind):
+    """Large scores: Q and K with standard deviation `std` give scores of standard deviation
+    std² (4 to 36), so a row's running max moves by more than the lazy-rescale threshold
+    (2^8 in probability) many times along its walk and most probabilities underflow to zero,
+    mixed with the -inf of masked entries.  The float32 case stays at std 2: float32 rounding of
+    the exponent argument grows with the score's size, so larger scores would test float32
+    itself against the 1e-4 bar rather than the kernel.  O, LSE and the gradients against the oracle on the
+    same rounded inputs; where an exact bf16 gradient reaches 4, dO is scaled by a power of two
+    (exact in both paths) so bf16 storage still resolves the 2e-2 bar."""
+    B, H, nq, nk = 1, 2, 517, 517
+    d = 128 if dtype == "bf16" else 64
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    r = rng(77, int(std), len(kind))
+    v = make_mask(kind, r, nq, nk)
+    g = torch.Generator().manual_seed(int(10 * std) + len(kind))
+    q, k = (std * torch.randn(B, H, n, d, generator=g) for n in (nq, nk))
+    vv, do = (torch.randn(B, H, n, d, generator=g) for n in (nk, nq))
+    q, k, vv, do = (x.to(td) for x in (q, k, vv, do))
+    scale = 1.0 / math.sqrt(d)
+    O, LSE = oracle.attention_fwd(q, k, vv, v, np.float32(scale))
+    dQ, dK, dV = oracle.attention_bwd(q, k, vv, do, v, np.float32(scale))
+    if dtype == "bf16":
+        peak = max(np.abs(x).max(initial=0.0) for x in (dQ, dK, dV))
+        if peak >= 4.0:
+            c = 2.0 ** -math.ceil(math.log2(peak / 4.0) + 1e-12)
+            do = (do.to(torch.float32) * c).to(td)
+            dQ, dK, dV = dQ * c, dK * c, dV * c
+    dvec = [dev_i32(x) for x in v]
+    qd, kd, vd, dod = (x.cuda() for x in (q, k, vv, do))
+    print(f"peaked scores {dtype} std={std} mask={kind}", flush=True)
+    o, lse = fm.fwd(qd, kd, vd, *dvec, scale)
+    dq, dk, dv = fm.bwd(qd, kd, vd, o, dod, lse, *dvec, scale)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    assert_close("O", f64(o), O, tol)
+    assert_lse(f64(lse), LSE)
+    assert_close("dQ", f64(dq), dQ, tol)
+    assert_close("dK", f64(dk), dK, tol)
+    assert_close("dV", f64(dv), dV, tol)
