@@ -37,6 +37,8 @@
 
 namespace fm {
 
+FM_STAMP_ARRAY(g_stamps_dkdv, flashmask_debug_stamps_dkdv)
+
 namespace {
 
 // Two shapes of the kernel (NG key groups of 32 keys, a P wave and a dS wave each; NBUF tile
@@ -103,6 +105,7 @@ __global__ __launch_bounds__(128 * NG, sizeof(T) == 2 ? 4 / NG : 1) void attn_bw
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
 
+  WgStamps stamps;  // workgroup timeline (debug build only)
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -136,6 +139,7 @@ __global__ __launch_bounds__(128 * NG, sizeof(T) == 2 ? 4 / NG : 1) void attn_bw
 #pragma unroll
       for (int i = 0; i < 8; ++i) p[i] = make_uint4(0u, 0u, 0u, 0u);
     }
+    stamps.store(FM_STAMP_BUF(g_stamps_dkdv), 0);
     return;
   }
 
@@ -465,6 +469,7 @@ __global__ __launch_bounds__(128 * NG, sizeof(T) == 2 ? 4 / NG : 1) void attn_bw
       wait_vmem();
     }
     lds_barrier();
+    stamps.first_tile();
   }
   f32x16 dp_prev = {};  // dS wave: dP of the pending unit
   auto walk = [&](auto role) {
@@ -536,6 +541,7 @@ __global__ __launch_bounds__(128 * NG, sizeof(T) == 2 ? 4 / NG : 1) void attn_bw
     walk(std::true_type{});
   else
     walk(std::false_type{});
+  stamps.walk_done();
   // The last two tile steps loaded a tile again into a free buffer; those loads must land before
   // the workgroup ends and its LDS is handed to another.
   wait_vmem();
@@ -568,6 +574,7 @@ __global__ __launch_bounds__(128 * NG, sizeof(T) == 2 ? 4 / NG : 1) void attn_bw
         }
       }
   }
+  stamps.store(FM_STAMP_BUF(g_stamps_dkdv), total);
 }
 
 template <typename T, int D, int NG, int NBUF>

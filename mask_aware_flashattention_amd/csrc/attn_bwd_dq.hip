@@ -23,6 +23,8 @@
 
 namespace fm {
 
+FM_STAMP_ARRAY(g_stamps_dq, flashmask_debug_stamps_dq)
+
 namespace {
 
 template <typename T, int D>
@@ -69,6 +71,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
       return mw1;
   };
 
+  WgStamps stamps;  // workgroup timeline (debug build only)
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -119,6 +122,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
         a.lse2[row_idx] = lse2;
       }
     }
+    stamps.store(FM_STAMP_BUF(g_stamps_dq), 0);
     return;
   }
 
@@ -238,6 +242,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
     const auto other = std::integral_constant<int, buf ^ 1>{};
     wait_vmem();      // this wave's loads of tile `it` have landed in LDS
     __syncthreads();  // ... everyone's, and the mask words
+    if (it == 0) stamps.first_tile();
     MaskKey mk{0, 0, 0, 0, false};
     if (next_test) mk = mask_load(next);
     // The last tile stages its own rows again into the free buffer, which is never read: the
@@ -346,6 +351,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
     body(it + 1, std::integral_constant<int, 1>{});
   }
   if (it < cnt) body(it, std::integral_constant<int, 0>{});
+  stamps.walk_done();
   wait_vmem();  // the last tile's extra loads land before the workgroup's LDS is released
 
   if (row_ok) {
@@ -368,6 +374,7 @@ __global__ __launch_bounds__(256, 2) void attn_dq_kernel(DqArgs a) {
         }
       }
   }
+  stamps.store(FM_STAMP_BUF(g_stamps_dq), cnt);
 }
 
 template <typename T, int D>

@@ -31,6 +31,8 @@
 
 namespace fm {
 
+FM_STAMP_ARRAY(g_stamps_fwd, flashmask_debug_stamps_fwd)
+
 namespace {
 
 template <typename T, int D>
@@ -77,6 +79,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       return mw1;
   };
 
+  WgStamps stamps;  // workgroup timeline (debug build only)
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -117,6 +120,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
       for (int i = 0; i < 8; ++i) p[i] = make_uint4(0u, 0u, 0u, 0u);
       if (g == 0) lse_row[q_row] = -INFINITY;
     }
+    stamps.store(FM_STAMP_BUF(g_stamps_fwd), 0);
     return;
   }
 
@@ -229,6 +233,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     const bool next_test = has_next && is_test(next);
     wait_vmem();      // this wave's loads of tile `it` have landed in LDS
     __syncthreads();  // ... everyone's, and the mask words; the other buffer is free
+    if (it == 0) stamps.first_tile();
     MaskKey mk{0, 0, 0, 0, false};
     if (next_test) mk = mask_load(next);
 
@@ -340,6 +345,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
     body(it + 1, std::integral_constant<int, 1>{});
   }
   if (it < cnt) body(it, std::integral_constant<int, 0>{});
+  stamps.walk_done();
   wait_vmem();  // the last tile's extra loads land before the workgroup's LDS is released
 
   const float l = pair_sum32(l_run);
@@ -364,6 +370,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdArgs a) {
         }
       }
   }
+  stamps.store(FM_STAMP_BUF(g_stamps_fwd), cnt);
 }
 
 }  // namespace

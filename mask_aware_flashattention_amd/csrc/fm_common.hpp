@@ -180,6 +180,59 @@ __device__ inline int xcd_contiguous_index(int bid, int nwg) {
   return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+// ---- workgroup timeline (debug build only) -----------------------------------------------------
+// Built with FM_WG_STAMPS (libflashmask_stamps.so), each attention workgroup records, through
+// thread 0, the real-time counter (s_memrealtime, 100 MHz) at its start, after its first tile's
+// barrier and after its tile walk, then at its end: slot blockIdx.x of a per-kernel device array
+// of kStampSlots * 8 words gets {start, first tile, walk done, end, HW_ID | XCC_ID << 32, tiles}.
+// In the default build every member is empty and the compiler removes the calls.
+constexpr int kStampSlots = 1 << 16;
+struct WgStamps {
+#ifdef FM_WG_STAMPS
+  unsigned long long t0, t1 = 0, t2 = 0;
+  __device__ WgStamps() : t0(__builtin_amdgcn_s_memrealtime()) {}
+  __device__ void first_tile() { t1 = __builtin_amdgcn_s_memrealtime(); }
+  __device__ void walk_done() { t2 = __builtin_amdgcn_s_memrealtime(); }
+  __device__ void store(unsigned long long* buf, int tiles) const {
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)kStampSlots) {
+      const unsigned long long t3 = __builtin_amdgcn_s_memrealtime();
+      const unsigned hw = __builtin_amdgcn_s_getreg(4 | (31 << 11));    // HW_ID
+      const unsigned xcc = __builtin_amdgcn_s_getreg(20 | (31 << 11));  // XCC_ID
+      unsigned long long* p = buf + (size_t)blockIdx.x * 8;
+      p[0] = t0;
+      p[1] = t1;
+      p[2] = t2;
+      p[3] = t3;
+      p[4] = hw | ((unsigned long long)xcc << 32);
+      p[5] = (unsigned long long)tiles;
+    }
+  }
+#else
+  __device__ void first_tile() {}
+  __device__ void walk_done() {}
+  __device__ void store(unsigned long long*, int) const {}
+#endif
+};
+// The per-kernel array behind WgStamps::store and the host call that copies it out (debug build
+// only; declared in include/flashmask_debug.h).
+#ifdef FM_WG_STAMPS
+#define FM_STAMP_ARRAY(name, getter)                                                           \
+  __device__ unsigned long long name[kStampSlots * 8];                                         \
+  }                                                                                            \
+  extern "C" int getter(void* host, size_t bytes) {                                            \
+    if (!host || bytes > sizeof(unsigned long long) * fm::kStampSlots * 8) return -1;          \
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(fm::name), bytes, 0, hipMemcpyDeviceToHost) == \
+                   hipSuccess                                                                  \
+               ? 0                                                                             \
+               : -1;                                                                           \
+  }                                                                                            \
+  namespace fm {
+#define FM_STAMP_BUF(name) name
+#else
+#define FM_STAMP_ARRAY(name, getter)
+#define FM_STAMP_BUF(name) nullptr
+#endif
+
 // ---- raw buffer loads: out-of-range offsets return zeros, so tails need no branches ----------
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 

@@ -326,3 +326,28 @@ def test_noalloc_checks(lib):
     assert call(shape(d=64)) == FM_ERR_UNSUPPORTED
     assert call(shape(nq=0)) == FM_ERR_SHAPE
     assert call(shape(), q=NUL) == FM_ERR_NULL   # before the device is touched
+
+
+def test_debug_library_exports_the_stamp_calls_and_the_abi():
+    """The timeline build (libflashmask_stamps.so) exports everything include/flashmask.h
+    declares plus the three calls of include/flashmask_debug.h, which the default library
+    lacks; a null or oversized copy request is refused before any device work."""
+    from mask_aware_flashattention_amd import build
+    from mask_aware_flashattention_amd.wg_timeline import LIB_STAMPS
+    if not os.path.exists(LIB_STAMPS):
+        build.build(stamps=True)
+    dbg = ctypes.CDLL(LIB_STAMPS)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "flashmask_debug.h")).read(),
+                  flags=re.S)
+    debug_names = sorted(set(re.findall(r"\b(flashmask_\w+)\s*\(", text)))
+    assert debug_names == ["flashmask_debug_stamps_dkdv", "flashmask_debug_stamps_dq",
+                           "flashmask_debug_stamps_fwd"]
+    for n in declared_functions() + debug_names:
+        assert hasattr(dbg, n), n
+    plain = ctypes.CDLL(_lib.LIB_PATH)
+    for n in debug_names:
+        assert not hasattr(plain, n), n
+        f = getattr(dbg, n)
+        f.restype, f.argtypes = ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t]
+        assert f(None, 8) == -1
+        assert f(ctypes.c_void_p(0x1000), (1 << 16) * 8 * 8 + 8) == -1
